@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Decode benchmark: shared-routing sparse attention at 128K context.
+
+Workload (decode_128k_b8): 8 independent sequences at 131072 tokens, one
+routing step per sequence per decode step (d_idx = 64, bf16, top-2048)
+shared by 16 layers of GQA attention (32 query / 8 KV heads, head dim 128,
+bf16).  Each step appends one K_idx/K/V row per sequence (the KV cache the
+self-decoder would write), routes, and attends in all 16 layers: one pass of
+the whole hot path.  Inputs are seeded synthetic tensors already resident in
+HBM when timing starts.
+
+Prints one JSON line: decode tokens/s (8 tokens per step), the step's
+fraction of HBM peak, the attention kernel against the HBM roofline, and the
+CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def attn_bytes(L, B, M, Hq, Hkv, D, k, esize=2):
+    """Algorithmic bytes of one sparse-attention launch: the gathered K and V
+    rows (k per row, all KV heads, every layer), q in, out, index lists."""
+    gathered = L * B * M * k * Hkv * D * esize * 2
+    q_out = 2 * L * B * M * Hq * D * esize
+    lists = B * M * (k + 1) * 4
+    return gathered + q_out + lists
+
+
+def route_bytes(B, M, n, d, k, esize=2):
+    """Algorithmic bytes of one routing call: scan every visible routing key
+    once, read the queries, write the index lists and counts."""
+    return B * n * d * esize + B * M * d * esize + B * M * (k + 1) * 4
+
+
+def cpu_baseline(wl, K_idx, Kc, Vc, q_idx, q, n, budget_s):
+    """Time the CPU oracle (as written) on a bounded sample of decode
+    sequence-steps: routing over all n keys plus attention in all layers."""
+    import numpy as np
+    from oracle import clsa_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    affinity = len(os.sched_getaffinity(0))
+    # host copies are input preparation, done before the clock starts
+    K_np = [K_idx[b, :n].double().cpu().numpy() for b in range(wl.B)]
+    q_np = q_idx.double().cpu().numpy()
+    qa = [q[l].double().cpu().numpy() for l in range(wl.L)]
+    done, t_tot = 0, 0.0
+    for b in range(wl.B):
+        t0 = time.perf_counter()
+        s = O.route_scores(q_np[b, 0], K_np[b], n)
+        sel = O.topk_select(s, wl.k)
+        t_route = time.perf_counter() - t0
+        import torch
+        selt = torch.from_numpy(sel).to(Kc.device)
+        Kr = [Kc[l, b][selt].double().cpu().numpy() for l in range(wl.L)]
+        Vr = [Vc[l, b][selt].double().cpu().numpy() for l in range(wl.L)]
+        t0 = time.perf_counter()
+        sc = 1.0 / math.sqrt(wl.D)
+        G = wl.Hq // wl.Hkv
+        for l in range(wl.L):
+            for h in range(wl.Hq):
+                O.attend_head(qa[l][b, 0, h], Kr[l][:, h // G, :], Vr[l][:, h // G, :], sc)
+        t_attn = time.perf_counter() - t0
+        t_tot += t_route + t_attn
+        done += 1
+        if t_tot >= budget_s:
+            break
+    return {
+        "value": done / t_tot,
+        "unit": "tokens/s",
+        "cores": blas_threads,
+        "kind": "oracle",
+        "sample": (f"{done} sequence-steps of {wl.name} (one decode token each: fp64 routing "
+                   f"over {n} keys, exact top-{wl.k}, attention in {wl.L} layers x {wl.Hq} "
+                   f"heads); NumPy BLAS threads={blas_threads}, affinity cpus={affinity}"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_128k_b8")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of CPU oracle work in the baseline sample (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sequences shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    clsa.load_library()
+    base = gen.WORKLOADS[args.workload]
+    total_steps = args.warmup + args.steps
+    wl = base.with_(n_cap=base.n_ctx + total_steps)
+    N0 = wl.n_ctx
+
+    # ---- inputs, resident in HBM before timing ----
+    K_idx, u, _ = gen.gen_routing_keys(wl, dev)
+    Kc, Vc = gen.gen_kv(wl, dev)
+    new_kidx, new_k, new_v = gen.gen_append_rows(wl, total_steps, dev)
+    q_idx_all, q_all = [], []
+    for t in range(total_steps):
+        qi = gen.gen_routing_query(wl, u, t, dev)
+        q_idx_all.append(qi)
+        q_all.append(gen.gen_attn_query(wl, qi, t, dev))
+    n_ctx_all = torch.tensor([[N0 + t + 1] * wl.B for t in range(total_steps)],
+                             dtype=torch.int32, device=dev)
+    idx = torch.empty((wl.B, 1, wl.k), dtype=torch.int32, device=dev)
+    counts = torch.empty((wl.B, 1), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.L, wl.B, 1, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    ws_r = torch.empty(clsa.route_workspace_size(wl.B, 1, wl.d, wl.n_cap, wl.k, wl.k,
+                                                 torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, clsa.sparse_attn_workspace_size(wl.L, wl.B, 1, wl.Hq, wl.Hkv, wl.D,
+                                                              wl.k, torch.bfloat16)),
+                       dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = {"route": [], "attn": []}
+
+    def step(t, timed):
+        pos = N0 + t
+        K_idx[:, pos].copy_(new_kidx[t])          # append (the self-decoder's KV write)
+        Kc[:, :, pos].copy_(new_k[t])
+        Vc[:, :, pos].copy_(new_v[t])
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e2 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        clsa.route(q_idx_all[t], K_idx, wl.k, n_ctx=n_ctx_all[t], idx=idx, counts=counts,
+                   ws=ws_r)
+        if timed:
+            e1.record(stream)
+        clsa.sparse_attn(q_all[t], Kc, Vc, idx, counts, out=out, ws=ws_a)
+        if timed:
+            e2.record(stream)
+            ev["route"].append((e0, e1))
+            ev["attn"].append((e1, e2))
+
+    for t in range(args.warmup):
+        step(t, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(args.warmup, total_steps):
+        step(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert int(counts.min()) == wl.k and int(counts.max()) == wl.k
+
+    ms_step = wall * 1e3 / args.steps
+    tokens = wl.B * args.steps
+    route_ms = sum(a.elapsed_time(b) for a, b in ev["route"]) / args.steps
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev["attn"]) / args.steps
+    n_mid = N0 + args.warmup + args.steps // 2 + 1
+    a_bytes = attn_bytes(wl.L, wl.B, 1, wl.Hq, wl.Hkv, wl.D, wl.k)
+    r_bytes = route_bytes(wl.B, 1, n_mid, wl.d, wl.k)
+    app_bytes = wl.B * (wl.d * 2 + wl.L * 2 * wl.Hkv * wl.D * 2) * 2  # read staged + write
+    step_bytes = a_bytes + r_bytes + app_bytes
+    achieved = a_bytes / (attn_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": "decode tokens/s at 128K ctx, k=2048, 16 shared-routing layers; % HBM peak",
+        "value": tokens / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.B, "n_ctx": N0, "k": wl.k,
+                   "layers": wl.L, "d_idx": wl.d, "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "head_dim": wl.D, "append_per_step": 1},
+        "step_hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "step_breakdown_ms": {"route_call": route_ms, "attn_call": attn_ms,
+                              "append_and_gaps": ms_step - route_ms - attn_ms},
+        "roofline": {"kernel": "attn_mfma<4,128> (clsa_sparse_attn call, 16 layers)",
+                     "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": a_bytes},
+        "route_roofline": {"achieved": r_bytes / (route_ms * 1e-3) / 1e9, "unit": "GB/s",
+                           "frac": r_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                           "algorithmic_bytes_per_call": r_bytes},
+    }
+    if args.cpu_budget > 0:
+        t = total_steps - 1
+        res["cpu_baseline"] = cpu_baseline(wl, K_idx, Kc, Vc, q_idx_all[t], q_all[t],
+                                           N0 + t + 1, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,155 @@
+/*
+ * clsa.h - C ABI of libclsa, shared-routing sparse decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (CLSA explainer, ai-papers.net, "CLSAとは？
+ * ルーティング共有で128Kコンテキスト推論を17倍高速化するスパースアテンション",
+ * section "CLSAの仕組み"): for every query token a single routing step picks
+ * the top-k positions of the KV cache once, and every cross-decoder layer
+ * reuses that one index list to run softmax attention over only those rows.
+ * Section "計算コストの削減効果" of the same page gives the reason: routing is
+ * paid once per token (cost ~ N) instead of once per layer (~ L*N).
+ * The threshold variant follows the Louver summary (gist.science,
+ * "技術サマリー：スパースアテンションを範囲検索問題として捉える",
+ * section "1. 半空間範囲検索への帰着"): return every key whose inner product
+ * with the query is at least tau, with no false negatives.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers, 16-byte aligned, dense
+ *    row-major with the layouts given below.  Pointer arrays (one entry per
+ *    layer) are HOST arrays of device pointers.
+ *  - The caller owns every buffer.  The library allocates no device memory
+ *    and keeps no state between calls; scratch space comes from the caller's
+ *    workspace `ws` of at least the size returned by the matching
+ *    *_workspace_size function (same shape arguments).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on it and returns without synchronizing.  Calls that share
+ *    one workspace must be ordered (same stream, or synchronized).
+ *  - Arguments are validated on the host before anything is enqueued; a call
+ *    that returns an error has written nothing.  Conditions that can only
+ *    be seen on the device are reported through the outputs (see `counts`).
+ *  - q, q_idx, K, V and K_idx share the call's dtype; `out` has that dtype.
+ *    All arithmetic accumulates in fp32.  NaN/Inf inputs are undefined.
+ */
+#ifndef CLSA_H
+#define CLSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CLSA_VERSION 1
+/* Maximum number of layers one clsa_sparse_attn call accepts. */
+#define CLSA_MAX_LAYERS 64
+
+typedef enum clsa_dtype {
+  CLSA_F32 = 0,  /* IEEE binary32 */
+  CLSA_BF16 = 1  /* bfloat16, stored as uint16 bit patterns */
+} clsa_dtype;
+
+typedef enum clsa_status {
+  CLSA_OK = 0,
+  CLSA_ERR_INVALID = -1,           /* null pointer, bad shape or size */
+  CLSA_ERR_WORKSPACE = -2,         /* ws too small (or NULL with a nonzero need) */
+  CLSA_ERR_UNSUPPORTED_DTYPE = -3, /* dtype not CLSA_F32 / CLSA_BF16 */
+  CLSA_ERR_HIP = -4                /* a kernel launch failed */
+} clsa_status;
+
+/* Library version (CLSA_VERSION of the build). */
+int clsa_version(void);
+
+/* Static description of a status code. Never NULL. */
+const char* clsa_status_string(int status);
+
+/*
+ * clsa_route - top-k routing, computed once and shared by all layers.
+ * (CLSA explainer, section "CLSAの仕組み": top-k indices of the important KV
+ * pairs for each query token; k = 2048 is the pages' operating point.)
+ *
+ * Rows: R = B*M query rows; row (b, m) uses routing key set b.
+ *   q_idx  [B][M][d]      routing queries.
+ *   K_idx  [B][n_cap][d]  routing keys (one index head), n_cap slots per
+ *                         sequence; only the first n_ctx[b] are visible.
+ *   n_ctx  [B] int32, DEVICE, or NULL (then every sequence has n_cap keys).
+ *          Values are clamped to [0, n_cap].
+ *   q_pos0 -1 for decode (row (b, m) sees n_ctx[b] keys).  q_pos0 >= 0 marks
+ *          a prefill chunk: row m is the token at position q_pos0 + m and
+ *          sees keys 0 .. q_pos0 + m (causal, diagonal included), capped at
+ *          n_ctx[b].
+ *   k      routed tokens per row, k >= 1.
+ *   idx    [B][M][cap] int32 out: the selected key positions of the row, in
+ *          ascending order, then -1 up to cap.  cap >= k.
+ *   counts [B][M] int32 out: min(k, visible keys).
+ * Score: s_j = sum_i q_idx[i] * K_idx[j][i], fp32 accumulation of exact
+ * products (bf16 x bf16 is exact in fp32).  Selection: the counts largest
+ * scores; equal scores are taken in increasing j.  -0.0 equals +0.0.
+ * d must be 32, 64 or 128.
+ * Errors: CLSA_ERR_INVALID (null pointer, B/M/k < 1, d unsupported,
+ * n_cap < 1, cap < k, B*M*n_cap too large), CLSA_ERR_UNSUPPORTED_DTYPE,
+ * CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.
+ */
+size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, int k, int cap,
+                                 clsa_dtype dt);
+int clsa_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+               const int32_t* n_ctx, int64_t q_pos0, int k, clsa_dtype dt, int32_t* idx,
+               int32_t* counts, int cap, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * clsa_route_threshold - half-space selection with no false negatives.
+ * (Louver summary, section "1. 半空間範囲検索への帰着": every key with
+ * <q, k> >= tau is returned.)
+ *
+ * Same arguments as clsa_route, with
+ *   tau    [B][M] float, DEVICE: the row's threshold.
+ * Writes every visible j with s_j >= tau (fp32 score, fp32 compare) in
+ * ascending order.  counts[b][m] is the TRUE size of the set; if it exceeds
+ * cap only the first cap indices are written, and the caller re-runs with a
+ * larger cap (nothing is dropped silently).  Unused slots hold -1.
+ * Errors: as clsa_route (cap >= 1 instead of cap >= k).
+ */
+size_t clsa_route_threshold_workspace_size(int B, int M, int d, int64_t n_cap, int cap,
+                                           clsa_dtype dt);
+int clsa_route_threshold(const void* q_idx, const void* K_idx, int B, int M, int d,
+                         int64_t n_cap, const int32_t* n_ctx, int64_t q_pos0, const float* tau,
+                         clsa_dtype dt, int32_t* idx, int32_t* counts, int cap, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/*
+ * clsa_sparse_attn - softmax attention of every layer over the shared lists.
+ * (CLSA explainer, section "CLSAの仕組み": each cross-decoder layer reuses
+ * the one index list; the KV cache is the YOCO shared cache, so passing the
+ * same K/V pointer for every layer is the single-cache case.)
+ *
+ *   q[l]   [B][M][Hq][D]     query of layer l.
+ *   K[l], V[l] [B][n_cap][Hkv][D]  key/value cache of layer l, token-major.
+ *   idx    [B][M][cap] int32, counts [B][M] int32: as written by clsa_route
+ *          or clsa_route_threshold.  Row (b, m) attends over its first
+ *          min(counts, cap) entries; entries outside [0, n_cap) are skipped.
+ *   scale  logit scale; 0 means 1/sqrt(D).
+ *   out[l] [B][M][Hq][D] out, dtype of V.
+ *   lse    [L][B][M][Hq] float out (natural log-sum-exp of the scaled
+ *          logits), or NULL.
+ * Query head h reads KV head h / (Hq/Hkv) (grouped-query attention).
+ * An empty list gives out = 0 and lse = -inf.
+ * Constraints: 1 <= L <= CLSA_MAX_LAYERS, Hq % Hkv == 0, Hq/Hkv <= 16,
+ * Hkv <= 64, Hq <= 64, 8 <= D <= 256 and D % 8 == 0, Hq*D <= 8192.
+ * Errors: CLSA_ERR_INVALID, CLSA_ERR_UNSUPPORTED_DTYPE, CLSA_ERR_WORKSPACE,
+ * CLSA_ERR_HIP.
+ */
+size_t clsa_sparse_attn_workspace_size(int L, int B, int M, int Hq, int Hkv, int D, int cap,
+                                       clsa_dtype dt);
+int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D, const void* const* q,
+                     const void* const* K, const void* const* V, int64_t n_cap,
+                     const int32_t* idx, const int32_t* counts, int cap, float scale,
+                     clsa_dtype dt, void* const* out, float* lse, void* ws, size_t ws_bytes,
+                     void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CLSA_H */

@@ -1,1 +1,15 @@
-"""MI355X-native shared-routing sparse decode attention (CLSA)."""
+"""MI355X-native shared-routing sparse decode attention (CLSA).
+
+The compute path is libclsa.so (hand-written HIP for gfx950) behind a C ABI
+(include/clsa.h); `binding` marshals torch tensors into it.
+"""
+from .binding import (  # noqa: F401
+    ClsaError,
+    load_library,
+    route,
+    route_threshold,
+    route_threshold_workspace_size,
+    route_workspace_size,
+    sparse_attn,
+    sparse_attn_workspace_size,
+)

@@ -1,0 +1,110 @@
+// Device-side helpers shared by the libclsa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/clsa.h"
+
+#define CLSA_DEV __device__ __forceinline__
+
+namespace clsa {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bfloat16
+CLSA_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+CLSA_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// float -> bfloat16 with round-to-nearest-even; NaN stays a (quiet) NaN.
+CLSA_DEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------- order-preserving key
+// Monotone map float -> uint32: a > b  <=>  key(a) > key(b), and -0.0 maps to
+// the key of +0.0 so the two compare equal (as they do as floats).
+CLSA_DEV uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- wave ops
+CLSA_DEV int lane_id() { return (int)__lane_id(); }
+
+// number of set bits of `mask` in lanes below this one
+CLSA_DEV uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+CLSA_DEV float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
+  return v;
+}
+CLSA_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+CLSA_DEV uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m);
+  return v;
+}
+
+// inclusive prefix sum across the wave
+CLSA_DEV uint32_t wave_incl_scan(uint32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t t = __shfl_up(v, o);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// Block-wide inclusive scan of one value per thread.  `tmp` must hold one
+// uint32 per wave.  Every thread of the block must call it.
+template <int NT>
+CLSA_DEV uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
+  constexpr int NW = NT / kWave;
+  const int w = threadIdx.x / kWave;
+  uint32_t inc = wave_incl_scan(v);
+  if (lane_id() == kWave - 1) tmp[w] = inc;
+  __syncthreads();
+  uint32_t add = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i)
+    if (i < w) add += tmp[i];
+  __syncthreads();
+  return inc + add;
+}
+
+// ------------------------------------------------------------ memory order
+// Release this workgroup's prior global writes to the whole device, then
+// count one arrival on `ticket`; returns the previous count.
+CLSA_DEV uint32_t arrive_release(uint32_t* ticket) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+CLSA_DEV void acquire_device() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+CLSA_DEV uint32_t load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace clsa
+
+// Host helpers implemented in clsa_api.hip.
+namespace clsa {
+// Zero `bytes` (multiple of 4) at `p` with a fill kernel on `stream`.
+hipError_t zero_fill(void* p, size_t bytes, hipStream_t stream);
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+}  // namespace clsa

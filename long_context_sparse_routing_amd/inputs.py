@@ -36,6 +36,7 @@ __all__ = [
     "gen_threshold_inputs",
     "threshold_counts",
     "torch_dtype",
+    "gen_append_rows",
 ]
 
 
@@ -176,10 +177,8 @@ def gen_kv(wl: Workload, device, seed: int | None = None, layers=None):
     Kc = torch.empty((wl.L, wl.B, wl.n_cap, wl.Hkv, wl.D), dtype=dt, device=device)
     Vc = torch.empty_like(Kc)
     for l in lays:
-        gk = make_generator(device, seed_of(base, "K", l))
-        Kc[l] = _randn((wl.B, wl.n_cap, wl.Hkv, wl.D), gk, device, dtype=dt)
-        gv = make_generator(device, seed_of(base, "V", l))
-        Vc[l] = _randn((wl.B, wl.n_cap, wl.Hkv, wl.D), gv, device, dtype=dt)
+        Kc[l].normal_(generator=make_generator(device, seed_of(base, "K", l)))
+        Vc[l].normal_(generator=make_generator(device, seed_of(base, "V", l)))
     return Kc, Vc
 
 
@@ -256,3 +255,15 @@ def gen_threshold_inputs(wl: Workload, score_fn, device="cpu", seed: int | None 
         else:
             raise RuntimeError("threshold margin could not be cleared")
     return K.contiguous(), q.contiguous(), tau
+
+
+def gen_append_rows(wl: Workload, steps: int, device, seed: int | None = None):
+    """Rows appended by decode steps: K_idx rows [steps, B, d] and K/V rows
+    [steps, L, B, Hkv, D], all ~ N(0, 1) in the workload dtype."""
+    base = wl.base_seed if seed is None else seed
+    dt = torch_dtype(wl.dtype)
+    g = make_generator(device, seed_of(base, "append"))
+    new_kidx = _randn((steps, wl.B, wl.d), g, device).to(dt)
+    new_k = _randn((steps, wl.L, wl.B, wl.Hkv, wl.D), g, device, dtype=dt)
+    new_v = _randn((steps, wl.L, wl.B, wl.Hkv, wl.D), g, device, dtype=dt)
+    return new_kidx, new_k, new_v
