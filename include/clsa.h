@@ -148,6 +148,25 @@ int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D, const void* co
                      clsa_dtype dt, void* const* out, float* lse, void* ws, size_t ws_bytes,
                      void* stream);
 
+/*
+ * clsa_kv_append - write one new token's rows into preallocated caches.
+ * (CLSA explainer, section "CLSAの仕組み": the self-decoder writes the KV
+ * cache that every cross-decoder layer then reads.)  This is that per-step
+ * cache write, not part of routing or attention; it appends the routing key
+ * row and every layer's K and V rows of each sequence in one launch.
+ *
+ *   pos     [B] int32, DEVICE: slot written in sequence b; sequences whose
+ *           pos is outside [0, n_cap) are left untouched.
+ *   src_idx [B][d] -> dst_idx [B][n_cap][d]   (both NULL: no routing key)
+ *   src_k[l], src_v[l] [B][Hkv][D] -> K[l], V[l] [B][n_cap][Hkv][D],
+ *           l < L (L = 0: routing key only).  Pointer arrays are HOST arrays.
+ * Constraints: rows are 16-byte multiples (d*esize and Hkv*D*esize % 16 == 0).
+ * Errors: CLSA_ERR_INVALID, CLSA_ERR_UNSUPPORTED_DTYPE, CLSA_ERR_HIP.
+ */
+int clsa_kv_append(int L, int B, int Hkv, int D, int d, int64_t n_cap, const int32_t* pos,
+                   const void* src_idx, void* dst_idx, const void* const* src_k, void* const* K,
+                   const void* const* src_v, void* const* V, clsa_dtype dt, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -5,7 +5,12 @@ The compute path is libclsa.so (hand-written HIP for gfx950) behind a C ABI
 """
 from .binding import (  # noqa: F401
     ClsaError,
+    Prepared,
+    kv_append,
     load_library,
+    prepare_kv_append,
+    prepare_route,
+    prepare_sparse_attn,
     route,
     route_threshold,
     route_threshold_workspace_size,

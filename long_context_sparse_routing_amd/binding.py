@@ -64,6 +64,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.clsa_sparse_attn.restype = i32
     lib.clsa_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp, i32,
                                      ctypes.c_float, i32, vp, vp, vp, sz, vp]
+    lib.clsa_kv_append.restype = i32
+    lib.clsa_kv_append.argtypes = [i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32,
+                                   vp]
     if path is None:
         _lib = lib
     return lib
@@ -104,6 +107,22 @@ def _workspace(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor:
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
+class Prepared:
+    """A library call with every argument marshalled in advance (pointers,
+    sizes, stream).  Calling it only crosses into libclsa: meant for decode
+    loops that repeat the same call on the same buffers."""
+
+    def __init__(self, name: str, fn, args: tuple, result=None, keep=()):
+        self.name, self.fn, self.args, self.result = name, fn, args, result
+        self._keep = keep  # objects whose memory the pointers refer to
+
+    def __call__(self):
+        st = self.fn(*self.args)
+        if st != 0:
+            raise ClsaError(self.name, st)
+        return self.result
+
+
 def route_workspace_size(B, M, d, n_cap, k, cap, dtype) -> int:
     return int(load_library().clsa_route_workspace_size(B, M, d, n_cap, k, cap,
                                                          _dt(torch.empty(0, dtype=dtype))))
@@ -119,10 +138,11 @@ def sparse_attn_workspace_size(L, B, M, Hq, Hkv, D, cap, dtype) -> int:
         L, B, M, Hq, Hkv, D, cap, _dt(torch.empty(0, dtype=dtype))))
 
 
-def route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int, n_ctx: torch.Tensor | None = None,
-          q_pos0: int = -1, cap: int | None = None, idx: torch.Tensor | None = None,
-          counts: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
-    """clsa_route: q_idx [B, M, d], K_idx [B, n_cap, d] -> (idx [B, M, cap], counts [B, M])."""
+def prepare_route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int,
+                  n_ctx: torch.Tensor | None = None, q_pos0: int = -1, cap: int | None = None,
+                  idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None, stream=None) -> Prepared:
+    """clsa_route, marshalled: calling the result returns (idx, counts)."""
     lib = load_library()
     B, M, d = q_idx.shape
     n_cap = K_idx.shape[1]
@@ -136,12 +156,17 @@ def route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int, n_ctx: torch.Tensor 
     dt = _dt(q_idx)
     need = lib.clsa_route_workspace_size(B, M, d, n_cap, k, cap, dt)
     ws = _workspace(need, dev, ws)
-    st = lib.clsa_route(_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0, k, dt,
-                        _ptr(idx), _ptr(counts), cap, _ptr(ws), ws.numel() * ws.element_size(),
-                        _stream(stream))
-    if st != 0:
-        raise ClsaError("clsa_route", st)
-    return idx, counts
+    args = (_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0, k, dt, _ptr(idx),
+            _ptr(counts), cap, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return Prepared("clsa_route", lib.clsa_route, args, (idx, counts),
+                    (q_idx, K_idx, n_ctx, idx, counts, ws))
+
+
+def route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int, n_ctx: torch.Tensor | None = None,
+          q_pos0: int = -1, cap: int | None = None, idx: torch.Tensor | None = None,
+          counts: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """clsa_route: q_idx [B, M, d], K_idx [B, n_cap, d] -> (idx [B, M, cap], counts [B, M])."""
+    return prepare_route(q_idx, K_idx, k, n_ctx, q_pos0, cap, idx, counts, ws, stream)()
 
 
 def route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor, cap: int,
@@ -177,14 +202,10 @@ def _layers(x) -> list:
     return list(x)
 
 
-def sparse_attn(q, K, V, idx: torch.Tensor, counts: torch.Tensor, scale: float = 0.0,
-                out=None, want_lse: bool = False, ws: torch.Tensor | None = None, stream=None):
-    """clsa_sparse_attn over L layers.
-
-    q: [L, B, M, Hq, D] tensor or list of L [B, M, Hq, D]; K, V: [L, B, n_cap,
-    Hkv, D] or lists of [B, n_cap, Hkv, D].  Returns (out [L, B, M, Hq, D],
-    lse [L, B, M, Hq] or None).
-    """
+def prepare_sparse_attn(q, K, V, idx: torch.Tensor, counts: torch.Tensor, scale: float = 0.0,
+                        out=None, want_lse: bool = False, ws: torch.Tensor | None = None,
+                        stream=None) -> Prepared:
+    """clsa_sparse_attn, marshalled: calling the result returns (out, lse)."""
     lib = load_library()
     ql, Kl, Vl = _layers(q), _layers(K), _layers(V)
     L = len(ql)
@@ -211,9 +232,51 @@ def sparse_attn(q, K, V, idx: torch.Tensor, counts: torch.Tensor, scale: float =
     ka = arr(*[t.data_ptr() for t in Kl])
     va = arr(*[t.data_ptr() for t in Vl])
     oa = arr(*[t.data_ptr() for t in outl])
-    st = lib.clsa_sparse_attn(L, B, M, Hq, Hkv, D, qa, ka, va, n_cap, _ptr(idx), _ptr(counts),
-                              cap, float(scale), dt, oa, _ptr(lse), _ptr(ws),
-                              ws.numel() * ws.element_size(), _stream(stream))
-    if st != 0:
-        raise ClsaError("clsa_sparse_attn", st)
-    return out, lse
+    args = (L, B, M, Hq, Hkv, D, qa, ka, va, n_cap, _ptr(idx), _ptr(counts), cap, float(scale),
+            dt, oa, _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return Prepared("clsa_sparse_attn", lib.clsa_sparse_attn, args, (out, lse),
+                    (ql, Kl, Vl, idx, counts, out, lse, ws))
+
+
+def sparse_attn(q, K, V, idx: torch.Tensor, counts: torch.Tensor, scale: float = 0.0,
+                out=None, want_lse: bool = False, ws: torch.Tensor | None = None, stream=None):
+    """clsa_sparse_attn over L layers.
+
+    q: [L, B, M, Hq, D] tensor or list of L [B, M, Hq, D]; K, V: [L, B, n_cap,
+    Hkv, D] or lists of [B, n_cap, Hkv, D].  Returns (out [L, B, M, Hq, D],
+    lse [L, B, M, Hq] or None).
+    """
+    return prepare_sparse_attn(q, K, V, idx, counts, scale, out, want_lse, ws, stream)()
+
+
+def prepare_kv_append(pos: torch.Tensor, src_idx=None, dst_idx=None, src_k=None, K=None,
+                      src_v=None, V=None, stream=None) -> Prepared:
+    """clsa_kv_append, marshalled.  pos [B] int32; src_idx [B, d] ->
+    dst_idx [B, n_cap, d]; src_k/src_v [L, B, Hkv, D] (or lists) -> K/V
+    [L, B, n_cap, Hkv, D] (or lists)."""
+    lib = load_library()
+    B = pos.shape[0]
+    ks = _layers(src_k) if src_k is not None else []
+    vs = _layers(src_v) if src_v is not None else []
+    Kd = _layers(K) if K is not None else []
+    Vd = _layers(V) if V is not None else []
+    L = len(ks)
+    if not (len(vs) == len(Kd) == len(Vd) == L):
+        raise ValueError("src_k, K, src_v and V need the same number of layers")
+    ref = dst_idx if dst_idx is not None else Kd[0]
+    n_cap = ref.shape[1]
+    d = dst_idx.shape[2] if dst_idx is not None else 0
+    Hkv, D = (Kd[0].shape[2], Kd[0].shape[3]) if L else (0, 0)
+    _check_dev(pos, src_idx, dst_idx, *ks, *vs, *Kd, *Vd)
+    dt = _dt(ref)
+    arr = ctypes.c_void_p * max(L, 1)
+    mk = lambda ts: arr(*[t.data_ptr() for t in ts]) if ts else None  # noqa: E731
+    args = (L, B, Hkv, D, d, n_cap, _ptr(pos), _ptr(src_idx), _ptr(dst_idx), mk(ks), mk(Kd),
+            mk(vs), mk(Vd), dt, _stream(stream))
+    return Prepared("clsa_kv_append", lib.clsa_kv_append, args, None,
+                    (pos, src_idx, dst_idx, ks, vs, Kd, Vd))
+
+
+def kv_append(pos, src_idx=None, dst_idx=None, src_k=None, K=None, src_v=None, V=None,
+              stream=None):
+    prepare_kv_append(pos, src_idx, dst_idx, src_k, K, src_v, V, stream)()

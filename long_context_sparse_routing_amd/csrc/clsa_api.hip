@@ -24,7 +24,71 @@ hipError_t zero_fill(void* p, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
+struct AppendArgs {
+  const void* src[2 * CLSA_MAX_LAYERS + 1];
+  void* dst[2 * CLSA_MAX_LAYERS + 1];
+  const int32_t* pos;
+  int64_t n_cap;
+  int B;
+  int row_bytes_kv;   // Hkv * D * esize
+  int row_bytes_idx;  // d * esize
+  int n_kv;           // 2 * L
+};
+
+// blockIdx.x = tensor (K0, V0, K1, V1, ..., then the routing keys), y = sequence
+__global__ __launch_bounds__(128) void kv_append_kernel(AppendArgs a) {
+  const int t = blockIdx.x, b = blockIdx.y;
+  const int p = a.pos[b];
+  if (p < 0 || (int64_t)p >= a.n_cap) return;
+  const int rb = t < a.n_kv ? a.row_bytes_kv : a.row_bytes_idx;
+  const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.src[t]) +
+                                                    (size_t)b * rb);
+  uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.dst[t]) +
+                                        ((size_t)b * a.n_cap + p) * rb);
+  for (int i = threadIdx.x; i < rb / 16; i += blockDim.x) dst[i] = src[i];
+}
+
 }  // namespace clsa
+
+extern "C" int clsa_kv_append(int L, int B, int Hkv, int D, int d, int64_t n_cap,
+                              const int32_t* pos, const void* src_idx, void* dst_idx,
+                              const void* const* src_k, void* const* K,
+                              const void* const* src_v, void* const* V, clsa_dtype dt,
+                              void* stream) {
+  using namespace clsa;
+  if (dt != CLSA_F32 && dt != CLSA_BF16) return CLSA_ERR_UNSUPPORTED_DTYPE;
+  if (L < 0 || L > CLSA_MAX_LAYERS || B < 1 || B > 65535 || n_cap < 1 || !pos)
+    return CLSA_ERR_INVALID;
+  const int es = dt == CLSA_BF16 ? 2 : 4;
+  if ((src_idx == nullptr) != (dst_idx == nullptr)) return CLSA_ERR_INVALID;
+  if (src_idx && (d < 1 || (d * es) % 16 != 0)) return CLSA_ERR_INVALID;
+  if (L > 0 && (Hkv < 1 || D < 1 || ((int64_t)Hkv * D * es) % 16 != 0 || !src_k || !K ||
+                !src_v || !V))
+    return CLSA_ERR_INVALID;
+  AppendArgs a{};
+  int n = 0;
+  for (int l = 0; l < L; ++l) {
+    if (!src_k[l] || !K[l] || !src_v[l] || !V[l]) return CLSA_ERR_INVALID;
+    a.src[n] = src_k[l];
+    a.dst[n++] = K[l];
+    a.src[n] = src_v[l];
+    a.dst[n++] = V[l];
+  }
+  a.n_kv = n;
+  if (src_idx) {
+    a.src[n] = src_idx;
+    a.dst[n++] = dst_idx;
+  }
+  if (n == 0) return CLSA_OK;
+  a.pos = pos;
+  a.n_cap = n_cap;
+  a.B = B;
+  a.row_bytes_kv = Hkv * D * es;
+  a.row_bytes_idx = d * es;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)n, (unsigned)B), dim3(128), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
+}
 
 extern "C" int clsa_version(void) { return CLSA_VERSION; }
 

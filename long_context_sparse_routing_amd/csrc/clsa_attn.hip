@@ -7,19 +7,17 @@
 // Grid: (split, row, layer).  A split is TS consecutive entries of the row's
 // index list; each workgroup streams its entries in sub-blocks of 64
 // tokens with an online (running max / running sum) softmax and writes
-// either the final output (one split) or a partial (m, l, acc).  The last
-// split workgroup of a (layer, row) to arrive merges the partials with the
-// log-sum-exp rule (combine_row); no workgroup waits for another.
+// either the final output (one split) or a partial (m, l, acc) that
+// attn_combine merges with the log-sum-exp rule.  No workgroup waits for
+// another; the kernel boundary orders the merge.
 //
-// attn_mfma  (bf16, D = 64/128, Hq/Hkv <= 16): one wave per KV head.  The
-//            scores of the G query heads of that KV head against 16 gathered
-//            key rows are one v_mfma_f32_16x16x32_bf16 chain: the A operand is
-//            the G query rows (zero-padded to 16), the B operand is 16 bytes
-//            of each key row per lane, loaded straight from HBM.  P.V runs on
-//            the VALU: each lane owns 8 consecutive output dims of one token
-//            slot and accumulates all G heads, so every gathered V byte is
-//            read once and used G times.
-// attn_generic (fp32, or shapes the MFMA kernel does not take): plain VALU.
+// attn_bf16  (bf16, D = 64/128/256, Hq/Hkv in {1,2,4,8,16}): one workgroup per
+//            KV head and split, four waves over its tokens.  Every gathered K
+//            and V row is read once, as whole cache lines, and used by all G
+//            query heads of its KV head.  This is an HBM-bound gather (about
+//            4 flop per byte), so the dot products run on the VALU
+//            (v_dot2_f32_bf16) rather than being padded into MFMA tiles.
+// attn_generic (fp32, or shapes attn_bf16 does not take): plain VALU.
 #include "clsa_common.h"
 
 namespace clsa {
@@ -39,7 +37,6 @@ struct AttnArgs {
   float* lse;
   float* pacc;   // [L][R][S][Hq][D]
   float2* pml;   // [L][R][S][Hq]  (running max in log2 units, running sum)
-  uint32_t* ticket;  // [L][R] arrivals of split workgroups (zeroed per call)
   int64_t n_cap;
   int L, B, M, Hq, Hkv, D, cap, TS, S;
   float scale_log2;  // logit scale times log2(e)
@@ -82,10 +79,13 @@ CLSA_DEV void emit(const AttnArgs& a, int l, int r, int s, int nsplit, int h, in
 
 // ================================================================ combine
 // out = sum_s acc_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*), m* = max_s m_s;
-// lse = (m* + log2 sum_s l_s 2^(m_s - m*)) ln 2.  Run by the last split
-// workgroup of (l, r) after an acquire fence.
+// lse = (m* + log2 sum_s l_s 2^(m_s - m*)) ln 2.  Rows with one split were
+// finished by their only workgroup.
 template <typename T>
-CLSA_DEV void combine_row(const AttnArgs& a, int l, int r, int nsplit) {
+__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
+  const int r = blockIdx.x, l = blockIdx.y;
+  const int nsplit = row_splits(a, row_count(a, r));
+  if (nsplit == 1) return;
   const size_t base = ((size_t)l * a.B * a.M + r) * a.S;
   for (int i = threadIdx.x; i < a.Hq * a.D; i += blockDim.x) {
     const int h = i / a.D, d = i % a.D;
@@ -107,176 +107,223 @@ CLSA_DEV void combine_row(const AttnArgs& a, int l, int r, int nsplit) {
   }
 }
 
-// Called by every thread of a split workgroup after its partial is written.
-template <typename T>
-CLSA_DEV void finish_split(const AttnArgs& a, int l, int r, int nsplit, uint32_t* s_last) {
-  if (nsplit == 1) return;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    *s_last = (arrive_release(&a.ticket[(size_t)l * a.B * a.M + r]) == (uint32_t)(nsplit - 1));
-  __syncthreads();
-  if (!*s_last) return;
-  acquire_device();
-  combine_row<T>(a, l, r, nsplit);
+// ======================================================= gathered (bf16)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+CLSA_DEV float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// ============================================================ MFMA (bf16)
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Sum NV per-lane partials over each group of LANES consecutive lanes,
+// halving the values kept per lane at each butterfly step while more than
+// one is left.  Afterwards v[0 .. max(1, NV/LANES)) hold complete sums of
+// value indices base, base+1, ...
+template <int NV, int LANES, int M = LANES / 2, int C = NV>
+CLSA_DEV void group_reduce(float (&v)[NV], int lane, int& base) {
+  if constexpr (M >= 1) {
+    if constexpr (C > 1) {
+      constexpr int H = C / 2;
+      const bool up = (lane & M) != 0;
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float send = up ? v[i] : v[i + H];
+        const float keep = up ? v[i + H] : v[i];
+        v[i] = keep + __shfl_xor(send, M);
+      }
+      base += up ? H : 0;
+      group_reduce<NV, LANES, M / 2, H>(v, lane, base);
+    } else {
+      v[0] += __shfl_xor(v[0], M);
+      group_reduce<NV, LANES, M / 2, C>(v, lane, base);
+    }
+  }
+}
 
+constexpr int kWaves = 4;
+// scores of one workgroup live in LDS: G heads x TS tokens of fp32
+constexpr int kScoreFloats = 8192;
+__host__ __device__ constexpr int ts_max(int G) { return kScoreFloats / G; }
+
+// Workgroup = (split s, KV head g) x row r x layer l; blockIdx.x = s*Hkv + g.
+// Every lane owns 8 consecutive dims (16 bytes) of one token slot, so one
+// load instruction reads whole 256-byte K or V rows of 64/(D/8) tokens
+// (full cache lines, streaming hint).  Three phases, separated by barriers:
+//   A  scores: per token, the G query heads' partial dot products over the
+//      lane's 8 dims (v_dot2_f32_bf16), reduced across the row's lanes,
+//      written to LDS in log2 units (skipped rows -inf);
+//   B  softmax: exact per-head max, 2^(s - max) and sum over the split;
+//   C  P.V: each gathered V row updates all G heads; the 4 waves' sums
+//      meet in LDS.
 template <int G, int D>
-__global__ __launch_bounds__(512) void attn_mfma(AttnArgs a) {
-  constexpr int kSteps = D / 32;   // MFMA k-steps (32 dims each)
-  constexpr int kQuarter = D / 4;  // dims owned by one k-block of lanes
-  constexpr int kLPT = D / 8;      // PV lanes per token (8 dims each)
-  constexpr int kTPW = 64 / kLPT;  // PV tokens per wave pass
-  static_assert(G >= 1 && G <= 16, "group size");
-  static_assert(D == 64 || D == 128, "head dim");
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : (G <= 8 ? 3 : 2), 8)))
+void attn_bf16(AttnArgs a) {
+  constexpr int kLPT = D / 8;      // lanes per token row (8 dims each)
+  constexpr int kTPW = 64 / kLPT;  // token rows per wave load
+  constexpr int kTS = ts_max(G);
+  constexpr int kAB = 2;           // K rows in flight per lane
+  constexpr int kVB = 4;           // V rows in flight per lane
+  constexpr int kNR = G / kLPT > 0 ? G / kLPT : 1;  // sums per lane after the reduce
+  constexpr int kShare = kLPT / (G < kLPT ? G : kLPT);  // lanes holding the same sums
+  static_assert(G >= 1 && G <= 16 && (G & (G - 1)) == 0, "group size");
+  static_assert(D == 64 || D == 128 || D == 256, "head dim");
+  static_assert(kWaves * G * D <= kScoreFloats, "wave partials alias the scores");
 
-  __shared__ float sc_all[8][G][kTB];
-  __shared__ uint32_t s_last;
+  __shared__ float sc[G][kTS];     // scores, then probabilities, then wave partials
+  __shared__ int sidx[kTS];
+  constexpr int kHPW = (G + kWaves - 1) / kWaves;  // heads per wave in phase B
 
-  const int s = blockIdx.x, r = blockIdx.y, l = blockIdx.z;
+  const int g = blockIdx.x % a.Hkv, s = blockIdx.x / a.Hkv;
+  const int r = blockIdx.y, l = blockIdx.z;
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int W = blockDim.x / kWave;
   const int cnt = row_count(a, r);
   const int nsplit = row_splits(a, cnt);
   if (s >= nsplit) return;
   const int t_begin = s * a.TS;
-  int t_end = t_begin + a.TS;
-  t_end = t_end < cnt ? t_end : cnt;
+  int nt = cnt - t_begin;
+  nt = nt < a.TS ? nt : a.TS;  // tokens of this split, <= kTS
 
   const int b = r / a.M;
-  float (*sc)[kTB] = sc_all[w];
   const uint16_t* Kl = static_cast<const uint16_t*>(a.K[l]);
   const uint16_t* Vl = static_cast<const uint16_t*>(a.V[l]);
   const uint16_t* ql = static_cast<const uint16_t*>(a.q[l]);
-  const int32_t* irow = a.idx + (size_t)r * a.cap;
-  const size_t seq_base = (size_t)b * a.n_cap;
+  const int32_t* irow = a.idx + (size_t)r * a.cap + t_begin;
+  const size_t head_base = (size_t)b * a.n_cap * a.Hkv + g;  // row j -> (head_base + j*Hkv)*D
+  const int tq = lane / kLPT, ds = lane % kLPT;
 
-  const int kb = lane / 16, col = lane % 16;  // MFMA lane coordinates
-  const int tq = lane / kLPT, ds = lane % kLPT;  // PV lane coordinates
-
-  for (int g = w; g < a.Hkv; g += W) {
-    // A operand: query rows of this KV head's group, zero beyond G
-    bf16x8_t qa[kSteps];
+  for (int i = threadIdx.x; i < nt; i += blockDim.x) {
+    const int rw = irow[i];
+    sidx[i] = (rw < 0 || (int64_t)rw >= a.n_cap) ? -1 : rw;
+  }
+  // the lane's 8 dims of every query head of this KV head, as bf16 pairs
+  u32x4_t qw[G];
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (col < G) {
-        const size_t qo = (((size_t)r * a.Hq) + g * G + col) * D + kb * kQuarter + st * 8;
-        v = *reinterpret_cast<const u32x4_t*>(ql + qo);
-      }
-      qa[st] = __builtin_bit_cast(bf16x8_t, v);
+  for (int h = 0; h < G; ++h)
+    qw[h] = *reinterpret_cast<const u32x4_t*>(ql + (((size_t)r * a.Hq) + g * G + h) * D + ds * 8);
+  __syncthreads();
+
+  // ---- phase A: scores ----
+  const int ngroups = (nt + kTPW - 1) / kTPW;
+  for (int grp0 = w * kAB; grp0 < ngroups; grp0 += kWaves * kAB) {
+    u32x4_t kk[kAB];
+    int ts[kAB], rws[kAB];
+#pragma unroll
+    for (int u = 0; u < kAB; ++u) {
+      const int t = (grp0 + u) * kTPW + tq;
+      const int rw = t < nt ? sidx[t] : -1;
+      ts[u] = t;
+      rws[u] = rw;
+      kk[u] = load_stream16(Kl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
     }
-    float m_run[G], l_run[G], acc[G][8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      m_run[h] = -INFINITY;
-      l_run[h] = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-    }
-
-    for (int t0 = t_begin; t0 < t_end; t0 += kTB) {
-      const int nt = (t_end - t0) < kTB ? (t_end - t0) : kTB;
-      int myrow = -1;
-      if (lane < nt) myrow = irow[t0 + lane];
-      if (myrow < 0 || (int64_t)myrow >= a.n_cap) myrow = -1;
-
-      // ---- scores: 4 tiles of 16 tokens, one MFMA chain per tile ----
-      u32x4_t kv[4][kSteps];
-#pragma unroll
-      for (int tile = 0; tile < 4; ++tile) {
-        const int rw = __shfl(myrow, tile * 16 + col);
-        const size_t ro = ((seq_base + (size_t)(rw < 0 ? 0 : rw)) * a.Hkv + g) * D + kb * kQuarter;
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st)
-          kv[tile][st] = *reinterpret_cast<const u32x4_t*>(Kl + ro + st * 8);
-      }
-#pragma unroll
-      for (int tile = 0; tile < 4; ++tile) {
-        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < kSteps; ++st)
-          c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st],
-                                                      __builtin_bit_cast(bf16x8_t, kv[tile][st]),
-                                                      c, 0, 0, 0);
-        const int rw = __shfl(myrow, tile * 16 + col);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int h = kb * 4 + j;
-          if (h < G) sc[h][tile * 16 + col] = rw >= 0 ? c[j] * a.scale_log2 : -INFINITY;
-        }
-      }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-
-      // ---- online softmax, lane = token ----
-      float alpha[G];
+    for (int u = 0; u < kAB; ++u) {
+      float v[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float v = sc[h][lane];
-        const float mx = wave_max(v);
-        const float m_new = fmaxf(m_run[h], mx);
-        const float p = (m_new == -INFINITY) ? 0.f : exp2f(v - m_new);
-        const float sum = wave_sum(p);
-        alpha[h] = (m_new == -INFINITY) ? 1.f : exp2f(m_run[h] - m_new);
-        l_run[h] = l_run[h] * alpha[h] + sum;
-        m_run[h] = m_new;
-        sc[h][lane] = p;
+        float acc = dot2(kk[u][0], qw[h][0], 0.f);
+        acc = dot2(kk[u][1], qw[h][1], acc);
+        acc = dot2(kk[u][2], qw[h][2], acc);
+        v[h] = dot2(kk[u][3], qw[h][3], acc);
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      int base = 0;
+      group_reduce<G, kLPT>(v, lane, base);
+      if ((ds & (kShare - 1)) == 0 && ts[u] < nt) {
+#pragma unroll
+        for (int i = 0; i < kNR; ++i)
+          sc[base + i][ts[u]] = rws[u] >= 0 ? v[i] * a.scale_log2 : -INFINITY;
+      }
+    }
+  }
+  __syncthreads();
 
-      // ---- P.V: lane owns dims ds*8..ds*8+7 of tokens tq, tq+kTPW, ... ----
+  // ---- phase B: softmax per head over the split; wave w owns heads
+  //      w, w+4, ... and keeps their max and sum in registers ----
+  float hm[kHPW], hl[kHPW];
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= alpha[h];
-#pragma unroll 4
-      for (int i = 0; i < kTB / kTPW; ++i) {
-        const int t = tq + i * kTPW;
-        const int rw = __shfl(myrow, t);
-        const size_t ro = ((seq_base + (size_t)(rw < 0 ? 0 : rw)) * a.Hkv + g) * D + ds * 8;
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(Vl + ro);
-        float vf[8];
-        vf[0] = bf16_lo(v[0]); vf[1] = bf16_hi(v[0]);
-        vf[2] = bf16_lo(v[1]); vf[3] = bf16_hi(v[1]);
-        vf[4] = bf16_lo(v[2]); vf[5] = bf16_hi(v[2]);
-        vf[6] = bf16_lo(v[3]); vf[7] = bf16_hi(v[3]);
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = sc[h][t];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+  for (int i = 0; i < kHPW; ++i) {
+    const int h = w + i * kWaves;
+    float mx = -INFINITY, sum = 0.f;
+    if (h < G) {
+      for (int t = lane; t < nt; t += kWave) mx = fmaxf(mx, sc[h][t]);
+      mx = wave_max(mx);
+      if (mx != -INFINITY) {
+        for (int t = lane; t < nt; t += kWave) {
+          const float p = exp2f(sc[h][t] - mx);
+          sc[h][t] = p;
+          sum += p;
         }
       }
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      sum = wave_sum(sum);
     }
+    hm[i] = mx;
+    hl[i] = sum;
+  }
+  __syncthreads();
 
-    // reduce the kTPW token slots that share a dim slice
+  // ---- phase C: P.V (skipped rows have p = 0) ----
+  float acc[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int grp0 = w * kVB; grp0 < ngroups; grp0 += kWaves * kVB) {
+    u32x4_t vv[kVB];
+    int ts[kVB], rws[kVB];
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int t = (grp0 + u) * kTPW + tq;
+      const int rw = t < nt ? sidx[t] : -1;
+      ts[u] = t;
+      rws[u] = rw;
+      vv[u] = load_stream16(Vl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      float vf[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vf[2 * e] = bf16_lo(vv[u][e]);
+        vf[2 * e + 1] = bf16_hi(vv[u][e]);
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = rws[u] >= 0 ? sc[h][ts[u]] : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
+      }
+    }
+  }
+  // sum the token slots sharing a dim slice, then the 4 waves (in LDS)
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = acc[h][e];
+#pragma unroll
+      for (int m = kLPT; m < 64; m <<= 1) v += __shfl_xor(v, m);
+      acc[h][e] = v;
+    }
+  __syncthreads();  // every wave is done reading the probabilities
+  float* wacc = &sc[0][0];  // [4][G][D]
+  if (tq == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float v = acc[h][e];
+      for (int e = 0; e < 8; ++e) wacc[(w * G + h) * D + ds * 8 + e] = acc[h][e];
+  }
+  __syncthreads();
 #pragma unroll
-        for (int m = kLPT; m < 64; m <<= 1) v += __shfl_xor(v, m);
-        acc[h][e] = v;
+  for (int i = 0; i < kHPW; ++i) {
+    const int h = w + i * kWaves;
+    if (h < G) {
+      for (int d = lane; d < D; d += kWave) {
+        float o = 0.f;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v) o += wacc[(v * G + h) * D + d];
+        emit<uint16_t>(a, l, r, s, nsplit, g * G + h, d, o, hm[i], hl[i], d == 0);
       }
-    if (tq == 0) {
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          emit<uint16_t>(a, l, r, s, nsplit, g * G + h, ds * 8 + e, acc[h][e], m_run[h],
-                         l_run[h], ds == 0 && e == 0);
     }
   }
-  finish_split<uint16_t>(a, l, r, nsplit, &s_last);
 }
 
 // ============================================================ generic VALU
@@ -289,7 +336,6 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
   __shared__ float sc[kGenMaxHq * kTB];
   __shared__ int sidx[kTB];
   __shared__ float m_run[kGenMaxHq], l_run[kGenMaxHq], alpha[kGenMaxHq];
-  __shared__ uint32_t s_last;
 
   const int s = blockIdx.x, r = blockIdx.y, l = blockIdx.z;
   const int tid = threadIdx.x;
@@ -377,14 +423,13 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
       emit<T>(a, l, r, s, nsplit, h, d, acc[k], m_run[h], l_run[h], d == 0);
     }
   }
-  finish_split<T>(a, l, r, nsplit, &s_last);
 }
 
 // ================================================================== host
 struct Plan {
-  bool mfma;
-  int TS, S, W;
-  size_t o_ticket, ticket_bytes, o_pml, o_pacc, total;
+  bool fast;
+  int TS, S;
+  size_t o_pml, o_pacc, total;
 };
 
 bool attn_shape_ok(int L, int B, int M, int Hq, int Hkv, int D, int cap) {
@@ -399,25 +444,29 @@ bool attn_shape_ok(int L, int B, int M, int Hq, int Hkv, int D, int cap) {
 Plan make_plan(int L, int B, int M, int Hq, int Hkv, int D, int cap, clsa_dtype dt) {
   Plan p{};
   const int G = Hq / Hkv;
-  p.mfma = dt == CLSA_BF16 && (D == 64 || D == 128) &&
+  p.fast = dt == CLSA_BF16 && (D == 64 || D == 128 || (D == 256 && G <= 8)) &&
            (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);
-  p.W = Hkv < 8 ? Hkv : 8;
   const int64_t rows = (int64_t)L * B * M;
-  // enough workgroups to fill the chip, without splitting rows needlessly
+  // enough workgroups to fill the chip, without splitting rows needlessly;
+  // the bf16 kernel already runs one workgroup per KV head
   const int64_t target = 1024;
-  int64_t S = (target + rows - 1) / rows;
-  const int64_t maxS = (cap + kTB - 1) / kTB;
+  const int64_t per_split = p.fast ? rows * Hkv : rows;
+  int64_t S = (target + per_split - 1) / per_split;
+  const int64_t min_ts = p.fast ? kTB * kWaves : kTB;
+  const int64_t maxS = (cap + min_ts - 1) / min_ts;
   if (S > maxS) S = maxS;
   if (S < 1) S = 1;
+  if (p.fast) {  // a split's scores must fit the workgroup's LDS
+    const int64_t tsm = ts_max(G);
+    const int64_t need = (cap + tsm - 1) / tsm;
+    if (S < need) S = need;
+  }
   int64_t TS = (cap + S - 1) / S;
   TS = (TS + kTB - 1) / kTB * kTB;
   p.TS = (int)TS;
   p.S = (int)((cap + TS - 1) / TS);
   size_t o = 0;
   if (p.S > 1) {
-    p.o_ticket = o;
-    p.ticket_bytes = align_up((size_t)rows * 4, 256);
-    o += p.ticket_bytes;
     p.o_pml = o;
     o = align_up(o + (size_t)rows * p.S * Hq * sizeof(float2), 256);
     p.o_pacc = o;
@@ -428,9 +477,10 @@ Plan make_plan(int L, int B, int M, int Hq, int Hkv, int D, int cap, clsa_dtype 
 }
 
 template <int G>
-void launch_mfma_g(int D, dim3 grid, dim3 block, hipStream_t s, const AttnArgs& a) {
-  if (D == 128) hipLaunchKernelGGL((attn_mfma<G, 128>), grid, block, 0, s, a);
-  else hipLaunchKernelGGL((attn_mfma<G, 64>), grid, block, 0, s, a);
+void launch_fast_g(int D, dim3 grid, dim3 block, hipStream_t s, const AttnArgs& a) {
+  if (D == 128) hipLaunchKernelGGL((attn_bf16<G, 128>), grid, block, 0, s, a);
+  else if (D == 64) hipLaunchKernelGGL((attn_bf16<G, 64>), grid, block, 0, s, a);
+  else if constexpr (G <= 8) hipLaunchKernelGGL((attn_bf16<G, 256>), grid, block, 0, s, a);
 }
 
 }  // namespace
@@ -472,7 +522,6 @@ extern "C" int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D,
   if (p.S > 1) {
     a.pml = reinterpret_cast<float2*>(static_cast<char*>(ws) + p.o_pml);
     a.pacc = reinterpret_cast<float*>(static_cast<char*>(ws) + p.o_pacc);
-    a.ticket = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + p.o_ticket);
   }
   a.n_cap = n_cap;
   a.L = L;
@@ -489,21 +538,26 @@ extern "C" int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D,
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int R = B * M;
-  if (p.S > 1 && zero_fill(a.ticket, p.ticket_bytes, s) != hipSuccess) return CLSA_ERR_HIP;
   const dim3 grid((unsigned)p.S, (unsigned)R, (unsigned)L);
-  if (p.mfma) {
-    const dim3 block((unsigned)(64 * p.W));
+  if (p.fast) {
+    const dim3 block(64 * kWaves);
+    const dim3 mgrid((unsigned)(p.S * Hkv), (unsigned)R, (unsigned)L);
     switch (Hq / Hkv) {
-      case 1: launch_mfma_g<1>(D, grid, block, s, a); break;
-      case 2: launch_mfma_g<2>(D, grid, block, s, a); break;
-      case 4: launch_mfma_g<4>(D, grid, block, s, a); break;
-      case 8: launch_mfma_g<8>(D, grid, block, s, a); break;
-      default: launch_mfma_g<16>(D, grid, block, s, a); break;
+      case 1: launch_fast_g<1>(D, mgrid, block, s, a); break;
+      case 2: launch_fast_g<2>(D, mgrid, block, s, a); break;
+      case 4: launch_fast_g<4>(D, mgrid, block, s, a); break;
+      case 8: launch_fast_g<8>(D, mgrid, block, s, a); break;
+      default: launch_fast_g<16>(D, mgrid, block, s, a); break;
     }
   } else if (dt == CLSA_BF16) {
     hipLaunchKernelGGL(attn_generic<uint16_t>, grid, dim3(256), 0, s, a);
   } else {
     hipLaunchKernelGGL(attn_generic<float>, grid, dim3(256), 0, s, a);
+  }
+  if (p.S > 1) {
+    const dim3 cg((unsigned)R, (unsigned)L);
+    if (dt == CLSA_BF16) hipLaunchKernelGGL(attn_combine<uint16_t>, cg, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attn_combine<float>, cg, dim3(256), 0, s, a);
   }
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
 }

@@ -12,6 +12,15 @@ namespace clsa {
 
 constexpr int kWave = 64;
 
+// ------------------------------------------------------------ vector loads
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// 16-byte load with the non-temporal (streaming) hint, for data read once:
+// gathered K/V rows and the routing-key scan.
+CLSA_DEV u32x4_t load_stream16(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+
 // ---------------------------------------------------------------- bfloat16
 CLSA_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 CLSA_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

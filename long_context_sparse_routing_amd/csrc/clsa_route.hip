@@ -9,47 +9,40 @@
 // summary (gist.science, arXiv 2605.06763), section "1. 半空間範囲検索への帰着"
 // -- all keys with <q, k> >= tau.
 //
-// Kernels (grid = chunks x rows; a chunk is CH consecutive keys of a row):
+// Kernels (grid = chunks x rows; a chunk is CH consecutive keys of a row).
+// Workgroups never wait on each other; kernel boundaries order the passes.
 //   route_score    s_j = q . K_idx[j] (fp32 accumulation, coalesced 16-byte
 //                  loads + a butterfly reduce-scatter across the lanes of a
 //                  key row), stores order-preserving uint32 keys, and either
-//                  builds the row's 2048-bucket histogram of the top 11 key
-//                  bits (top-k) or counts keys >= key(tau) per chunk
-//                  (threshold).  The last workgroup of a row finishes the
-//                  row: it finds the bucket holding the k-th largest key, or
-//                  scans the per-chunk counts into output offsets.
-//   route_cands    (top-k) collects the keys of that bucket as candidates
-//                  (composite key: low 21 key bits, then inverted position so
-//                  lower positions win ties) and counts keys above it per
-//                  chunk; the last workgroup runs an exact LDS radix select
-//                  over the candidates and scans per-chunk output offsets.
-//   route_compact  writes selected positions in ascending order with wave
-//                  ballots and per-chunk offsets, pads with -1, sets counts.
-// Completion of a row is detected with a per-row arrival counter (release /
-// acquire at agent scope); no workgroup ever waits on another.
+//                  adds the chunk's histogram of the top 11 key bits to the
+//                  row's 2048-bucket histogram (top-k) or counts keys >=
+//                  key(tau) per chunk (threshold).
+//   route_cands    (top-k) finds the bucket T1 holding the k-th largest key
+//                  from the histogram, counts keys above T1 per chunk, and
+//                  stores the chunk's keys in T1 (ascending position) as
+//                  candidates: low 21 key bits, then the inverted position so
+//                  that lower positions win ties.
+//                  It also histograms key bits 20..10 of those candidates.
+//   route_select   (top-k, one workgroup per row) finds the second-level bin
+//                  T2 of the k-th largest key from that histogram; each thread
+//                  walks its own chunks' candidates once, counting those above
+//                  T2 and collecting those in T2 (typically a handful), which
+//                  are ranked pairwise (lower position wins ties, through the
+//                  composite).  It writes the composite threshold Tc and every
+//                  chunk's output offset.
+//   route_compact  writes the selected positions of its chunk in ascending
+//                  order with wave ballots from the chunk's offset; pads
+//                  with -1 and sets counts.
 #include "clsa_common.h"
 
 namespace clsa {
 namespace {
 
-constexpr int kNT = 256;             // threads per workgroup
-constexpr int kBuckets = 2048;       // histogram of the top 11 key bits
+constexpr int kNT = 256;          // threads per workgroup
+constexpr int kBuckets = 2048;    // histogram of the top 11 key bits
 constexpr int kBucketShift = 21;
 constexpr uint32_t kLowMask = (1u << kBucketShift) - 1u;
-constexpr int kMaxChunks = 4096;     // chunks per row (LDS table in route_cands)
-constexpr int kCandLds = 6144;       // candidates kept in LDS for the select
-
-enum : uint32_t { kModeTopk = 0, kModeAll = 1, kModeThresh = 2 };
-
-struct RowInfo {
-  uint32_t mode;
-  uint32_t n_vis;
-  uint32_t count;  // keys to emit (top-k) or true set size (threshold)
-  uint32_t T1;     // top-k: bucket of the count-th key; threshold: key(tau)
-  uint32_t r1;     // top-k: keys to take from bucket T1
-  uint32_t pad;
-  uint64_t Tc;     // top-k: composite key of the last taken candidate
-};
+constexpr int kMaxChunks = 4096;  // chunks per row
 
 struct RouteArgs {
   const void* q;          // [R][d]
@@ -63,15 +56,14 @@ struct RouteArgs {
   int B, M, k, cap;
   int CH, C;              // keys per chunk, chunks per row (max)
   // workspace
-  uint32_t* ticket1;      // [R]
-  uint32_t* ticket2;      // [R]
-  uint32_t* ccount;       // [R]
-  uint32_t* ghist;        // [R][2048]
-  RowInfo* info;          // [R]
-  uint32_t* cnt;          // [R][C] keys above T1 (top-k) / keys >= tau (threshold)
-  uint32_t* coff;         // [R][C] output offset of each chunk
+  uint32_t* ghist;        // [R][2048]   top 11 key bits (zeroed at the start of each call)
+  uint32_t* ghist2;       // [R][2048]   key bits 20..10 of the keys in bucket T1 (zeroed too)
+  uint32_t* rowsel;       // [R][4]      T1, r1, Tc (64-bit)
+  uint32_t* off;          // [R][C]      output offset of each chunk (top-k)
+  uint32_t* cgt;          // [R][C]      keys above T1 / keys >= tau, per chunk
+  uint32_t* ccnt;         // [R][C]      candidates per chunk
   uint32_t* keys;         // [R][n_cap]
-  uint64_t* cand;         // [R][n_cap]
+  uint64_t* cand;         // [R][n_cap]  chunk c's candidates at [c*CH, ...)
 };
 
 CLSA_DEV int64_t visible(const RouteArgs& a, int r) {
@@ -98,11 +90,11 @@ CLSA_DEV uint64_t composite(uint32_t key, uint32_t j) {
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int kPer16 = 4;
-  CLSA_DEV static float dot(const uint4 v, const float* qf) {
-    float s = qf[0] * __uint_as_float(v.x);
-    s = fmaf(qf[1], __uint_as_float(v.y), s);
-    s = fmaf(qf[2], __uint_as_float(v.z), s);
-    s = fmaf(qf[3], __uint_as_float(v.w), s);
+  CLSA_DEV static float dot(const u32x4_t v, const float* qf) {
+    float s = qf[0] * __uint_as_float(v[0]);
+    s = fmaf(qf[1], __uint_as_float(v[1]), s);
+    s = fmaf(qf[2], __uint_as_float(v[2]), s);
+    s = fmaf(qf[3], __uint_as_float(v[3]), s);
     return s;
   }
   CLSA_DEV static void load_q(const void* q, size_t off, float* qf) {
@@ -113,16 +105,16 @@ template <> struct Elem<float> {
 };
 template <> struct Elem<uint16_t> {
   static constexpr int kPer16 = 8;
-  CLSA_DEV static float dot(const uint4 v, const float* qf) {
+  CLSA_DEV static float dot(const u32x4_t v, const float* qf) {
     // bf16 x bf16 products are exact in fp32, so fma and mul+add agree.
-    float s = qf[0] * bf16_lo(v.x);
-    s = fmaf(qf[1], bf16_hi(v.x), s);
-    s = fmaf(qf[2], bf16_lo(v.y), s);
-    s = fmaf(qf[3], bf16_hi(v.y), s);
-    s = fmaf(qf[4], bf16_lo(v.z), s);
-    s = fmaf(qf[5], bf16_hi(v.z), s);
-    s = fmaf(qf[6], bf16_lo(v.w), s);
-    s = fmaf(qf[7], bf16_hi(v.w), s);
+    float s = qf[0] * bf16_lo(v[0]);
+    s = fmaf(qf[1], bf16_hi(v[0]), s);
+    s = fmaf(qf[2], bf16_lo(v[1]), s);
+    s = fmaf(qf[3], bf16_hi(v[1]), s);
+    s = fmaf(qf[4], bf16_lo(v[2]), s);
+    s = fmaf(qf[5], bf16_hi(v[2]), s);
+    s = fmaf(qf[6], bf16_lo(v[3]), s);
+    s = fmaf(qf[7], bf16_hi(v[3]), s);
     return s;
   }
   CLSA_DEV static void load_q(const void* q, size_t off, float* qf) {
@@ -133,7 +125,7 @@ template <> struct Elem<uint16_t> {
 };
 
 // U partial sums per lane, U consecutive lanes per key row.  After the
-// butterfly, lane with in-group position p holds the full sum of partial
+// butterfly, the lane with in-group position p holds the full sum of partial
 // index p.  The addition tree is the same for every partial index, so
 // identical key rows give bit-identical scores.
 template <int U>
@@ -151,8 +143,42 @@ CLSA_DEV float reduce_scatter(float (&v)[U], int lane) {
   return v[0];
 }
 
+// Sum over the first `n` entries of `arr` (global), result in every thread.
+CLSA_DEV uint32_t block_sum_prefix(const uint32_t* arr, int64_t n, uint32_t* tmp) {
+  uint32_t loc = 0;
+  for (int64_t i = threadIdx.x; i < n; i += kNT) loc += arr[i];
+  uint32_t tot = wave_sum_u32(loc);
+  const int w = threadIdx.x / kWave;
+  if (lane_id() == 0) tmp[w] = tot;
+  __syncthreads();
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kNT / kWave; ++i) s += tmp[i];
+  __syncthreads();
+  return s;
+}
+
+// Ordered compaction of one 256-key slice: returns this thread's slot among
+// the set predicates of the slice (ascending thread order) and the slice's
+// total in *total.
+CLSA_DEV uint32_t block_rank(bool p, uint32_t* wcnt, uint32_t* total) {
+  const int w = threadIdx.x / kWave;
+  const uint64_t mask = __ballot(p);
+  if (lane_id() == 0) wcnt[w] = (uint32_t)__popcll(mask);
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kNT / kWave; ++i) {
+    before += (i < w) ? wcnt[i] : 0u;
+    tot += wcnt[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + lanes_below(mask);
+}
+
 // ------------------------------------------------------------------- score
-template <typename T, int D, uint32_t MODE>
+template <typename T, int D, bool TOPK>
 __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
   constexpr int kEPL = Elem<T>::kPer16;        // elements per 16-byte segment
   constexpr int kLPR = D / kEPL;               // lanes per key row
@@ -160,34 +186,21 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
   constexpr int kU = kLPR;                     // loads per lane per wave pass
   static_assert(kLPR >= 2 && kLPR <= 32, "unsupported row width");
 
-  __shared__ uint32_t hist[kBuckets];
-  __shared__ uint32_t scan_tmp[kNT / kWave];
-  __shared__ uint32_t s_last;
+  __shared__ uint32_t hist[TOPK ? kBuckets : 1];
+  __shared__ uint32_t tmp[kNT / kWave];
 
   const int c = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int b = r / a.M;
   const int64_t n_vis = visible(a, r);
-  const int64_t nch = chunks_of(n_vis, a.CH);
-  if (c >= nch) return;
-
-  if (MODE == kModeTopk) {
-    const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
-    if (k_eff >= n_vis) {  // every visible key is selected: no scoring needed
-      if (c == 0 && tid == 0) {
-        RowInfo ri{};
-        ri.mode = kModeAll;
-        ri.n_vis = (uint32_t)n_vis;
-        ri.count = (uint32_t)n_vis;
-        a.info[r] = ri;
-      }
-      return;
-    }
+  if (c >= chunks_of(n_vis, a.CH)) return;
+  if (TOPK) {
+    if ((int64_t)a.k >= n_vis) return;  // every visible key is selected
     for (int i = tid; i < kBuckets; i += kNT) hist[i] = 0u;
     __syncthreads();
   }
   uint32_t tkey = 0;
-  if (MODE == kModeThresh) tkey = score_key(a.tau[r]);
+  if (!TOPK) tkey = score_key(a.tau[r]);
 
   const int grp = lane / kLPR, pos = lane % kLPR;
   float qf[kEPL];
@@ -202,12 +215,12 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
     const int64_t wbase = j0 + (int64_t)it * kNT + w * kWave;
     if (wbase >= n_vis) break;
     float part[kU];
-    uint4 v[kU];
+    u32x4_t v[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int64_t j = wbase + u * kKPI + grp;
       const int64_t jj = j < n_vis ? j : 0;
-      v[u] = *reinterpret_cast<const uint4*>(Kb + (size_t)jj * D * sizeof(T) + pos * 16);
+      v[u] = load_stream16(Kb + (size_t)jj * D * sizeof(T) + pos * 16);
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) part[u] = Elem<T>::dot(v[u], qf);
@@ -216,12 +229,12 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
     if (j < n_vis) {
       const uint32_t key = score_key(s);
       keys_row[j] = key;
-      if (MODE == kModeTopk) atomicAdd(&hist[key >> kBucketShift], 1u);
-      if (MODE == kModeThresh) n_ge += (key >= tkey) ? 1u : 0u;
+      if (TOPK) atomicAdd(&hist[key >> kBucketShift], 1u);
+      else n_ge += (key >= tkey) ? 1u : 0u;
     }
   }
 
-  if (MODE == kModeTopk) {
+  if (TOPK) {
     __syncthreads();
     uint32_t* gh = a.ghist + (size_t)r * kBuckets;
     for (int i = tid; i < kBuckets; i += kNT) {
@@ -230,101 +243,141 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
     }
   } else {
     const uint32_t tot = wave_sum_u32(n_ge);
-    if (lane == 0) scan_tmp[w] = tot;
+    if (lane == 0) tmp[w] = tot;
     __syncthreads();
     if (tid == 0) {
       uint32_t t = 0;
-      for (int i = 0; i < kNT / kWave; ++i) t += scan_tmp[i];
-      a.cnt[(size_t)r * a.C + c] = t;
-    }
-  }
-
-  __syncthreads();
-  if (tid == 0) s_last = (arrive_release(&a.ticket1[r]) == (uint32_t)(nch - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  acquire_device();
-
-  if (MODE == kModeTopk) {
-    // Find the bucket holding the k_eff-th largest key.  Thread t owns
-    // buckets 2047-8t .. 2040-8t (descending).
-    const uint32_t k_eff = (uint32_t)(a.k < n_vis ? a.k : n_vis);
-    const uint32_t* gh = a.ghist + (size_t)r * kBuckets;
-    uint32_t h[8], sum = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      h[i] = load_relaxed(&gh[kBuckets - 1 - 8 * tid - i]);
-      sum += h[i];
-    }
-    const uint32_t incl = block_incl_scan<kNT>(sum, scan_tmp);
-    const uint32_t excl = incl - sum;
-    if (excl < k_eff && k_eff <= incl) {
-      uint32_t acc = excl;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        if (acc + h[i] >= k_eff) {
-          RowInfo ri{};
-          ri.mode = kModeTopk;
-          ri.n_vis = (uint32_t)n_vis;
-          ri.count = k_eff;
-          ri.T1 = (uint32_t)(kBuckets - 1 - 8 * tid - i);
-          ri.r1 = k_eff - acc;
-          a.info[r] = ri;
-          break;
-        }
-        acc += h[i];
-      }
-    }
-  } else {
-    // Exclusive scan of the per-chunk counts -> output offsets.
-    const int per = (int)ceil_div64(nch, kNT);
-    const int64_t cs = (int64_t)tid * per;
-    uint32_t loc = 0;
-    for (int i = 0; i < per; ++i)
-      if (cs + i < nch) loc += load_relaxed(&a.cnt[(size_t)r * a.C + cs + i]);
-    const uint32_t incl = block_incl_scan<kNT>(loc, scan_tmp);
-    uint32_t run = incl - loc;
-    for (int i = 0; i < per; ++i) {
-      if (cs + i < nch) {
-        const uint32_t v = load_relaxed(&a.cnt[(size_t)r * a.C + cs + i]);
-        a.coff[(size_t)r * a.C + cs + i] = run;
-        run += v;
-      }
-    }
-    if (tid == kNT - 1) {
-      RowInfo ri{};
-      ri.mode = kModeThresh;
-      ri.n_vis = (uint32_t)n_vis;
-      ri.count = incl;
-      ri.T1 = tkey;
-      a.info[r] = ri;
+      for (int i = 0; i < kNT / kWave; ++i) t += tmp[i];
+      a.cgt[(size_t)r * a.C + c] = t;
     }
   }
 }
 
-// ------------------------------------------------- exact radix select (LDS)
-// rank-th largest (1-based) of n distinct 53-bit composites.  Values come
-// from LDS when they fit, else from global memory.
-CLSA_DEV uint64_t block_select_desc(const uint64_t* src, uint32_t n, uint32_t rank,
-                                    uint32_t* h256, uint32_t* scan_tmp, uint32_t* bcast) {
+// -------------------------------------------------------------- candidates
+// Bucket T1 holding the k_eff-th largest key and how many keys r1 to take
+// from it.  Thread t owns buckets 2047-8t .. 2040-8t (descending).
+CLSA_DEV void find_bucket(const uint32_t* gh, uint32_t k_eff, uint32_t* tmp, uint32_t* out2) {
+  const int tid = threadIdx.x;
+  uint32_t h[8], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    h[i] = gh[kBuckets - 1 - 8 * tid - i];
+    sum += h[i];
+  }
+  const uint32_t incl = block_incl_scan<kNT>(sum, tmp);
+  const uint32_t excl = incl - sum;
+  if (excl < k_eff && k_eff <= incl) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (acc + h[i] >= k_eff) {
+        out2[0] = (uint32_t)(kBuckets - 1 - 8 * tid - i);
+        out2[1] = k_eff - acc;
+        break;
+      }
+      acc += h[i];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kNT) void route_cands(RouteArgs a) {
+  __shared__ uint32_t tmp[kNT / kWave];
+  __shared__ uint32_t wcnt[kNT / kWave];
+  __shared__ uint32_t sel[2];
+
+  const int c = blockIdx.x, r = blockIdx.y;
+  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
+  const int64_t n_vis = visible(a, r);
+  if (c >= chunks_of(n_vis, a.CH)) return;
+  if ((int64_t)a.k >= n_vis) return;
+
+  find_bucket(a.ghist + (size_t)r * kBuckets, (uint32_t)a.k, tmp, sel);
+  const uint32_t T1 = sel[0];
+  if (c == 0 && tid == 0) {
+    a.rowsel[4 * r] = sel[0];
+    a.rowsel[4 * r + 1] = sel[1];
+  }
+
+  const uint32_t* keys_row = a.keys + (size_t)r * a.n_cap;
+  uint64_t* cand_chunk = a.cand + (size_t)r * a.n_cap + (size_t)c * a.CH;
+  const int64_t j0 = (int64_t)c * a.CH;
+  uint32_t gt = 0, ncand = 0;
+  for (int it = 0; it < a.CH / kNT; ++it) {
+    const int64_t jb = j0 + (int64_t)it * kNT;
+    if (jb >= n_vis) break;
+    const int64_t j = jb + tid;
+    const bool valid = j < n_vis;
+    const uint32_t key = valid ? keys_row[j] : 0u;
+    const uint32_t bk = key >> kBucketShift;
+    gt += (valid && bk > T1) ? 1u : 0u;
+    const bool isc = valid && bk == T1;
+    uint32_t tot;
+    const uint32_t slot = block_rank(isc, wcnt, &tot);
+    if (isc) {
+      cand_chunk[ncand + slot] = composite(key, (uint32_t)j);
+      atomicAdd(&a.ghist2[(size_t)r * kBuckets + ((key >> 10) & 2047u)], 1u);
+    }
+    ncand += tot;
+  }
+  const uint32_t gtt = wave_sum_u32(gt);
+  if (lane == 0) tmp[w] = gtt;
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t t = 0;
+    for (int i = 0; i < kNT / kWave; ++i) t += tmp[i];
+    a.cgt[(size_t)r * a.C + c] = t;
+    a.ccnt[(size_t)r * a.C + c] = ncand;
+  }
+}
+
+// ------------------------------------------------------------------ select
+// Index of the bin holding the rank-th largest element of a descending
+// histogram h[0..NB) (bin NB-1 holds the largest values); rank is 1-based.
+// Returns the bin and the rank left inside it.  Every thread must call.
+template <int NB>
+CLSA_DEV void find_bin_desc(const uint32_t* h, uint32_t rank, uint32_t* tmp, uint32_t* out2) {
+  constexpr int PER = NB / kNT;
+  const int tid = threadIdx.x;
+  uint32_t v[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    v[i] = h[NB - 1 - PER * tid - i];
+    sum += v[i];
+  }
+  const uint32_t incl = block_incl_scan<kNT>(sum, tmp);
+  const uint32_t excl = incl - sum;
+  if (excl < rank && rank <= incl) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (acc + v[i] >= rank) {
+        out2[0] = (uint32_t)(NB - 1 - PER * tid - i);
+        out2[1] = rank - acc;
+        break;
+      }
+      acc += v[i];
+    }
+  }
+  __syncthreads();
+}
+
+// rank-th largest (1-based) of distinct 42-bit composites, visited through
+// `visit(f)`, which calls f(v) once per element, split over threads.  Slow
+// path for degenerate inputs only.
+template <class Visit>
+CLSA_DEV uint64_t block_select_desc(Visit visit, uint32_t rank, uint32_t* h256, uint32_t* tmp,
+                                    uint32_t* bcast) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0, pmask = 0;
-  for (int shift = 48; shift >= 0; shift -= 8) {
+  for (int shift = 40; shift >= 0; shift -= 8) {
     h256[tid] = 0u;
     __syncthreads();
-    for (uint32_t i = tid; i < n; i += kNT) {
-      const uint64_t v = src[i];
+    visit([&](uint64_t v) {
       if ((v & pmask) == prefix) atomicAdd(&h256[(uint32_t)(v >> shift) & 255u], 1u);
-    }
+    });
     __syncthreads();
-    const uint32_t cnt = h256[255 - tid];  // digits in descending order
-    const uint32_t incl = block_incl_scan<kNT>(cnt, scan_tmp);
-    const uint32_t excl = incl - cnt;
-    if (excl < rank && rank <= incl) {
-      bcast[0] = 255u - (uint32_t)tid;
-      bcast[1] = rank - excl;
-    }
-    __syncthreads();
+    find_bin_desc<256>(h256, rank, tmp, bcast);
     prefix |= (uint64_t)bcast[0] << shift;
     pmask |= (uint64_t)0xFFu << shift;
     rank = bcast[1];
@@ -333,141 +386,191 @@ CLSA_DEV uint64_t block_select_desc(const uint64_t* src, uint32_t n, uint32_t ra
   return prefix;
 }
 
-// -------------------------------------------------------------- candidates
-__global__ __launch_bounds__(kNT) void route_cands(RouteArgs a) {
-  __shared__ uint64_t cbuf[kCandLds];
+constexpr int kSmall = 256;  // boundary-bin candidates ranked pairwise
+
+__global__ __launch_bounds__(kNT) void route_select(RouteArgs a) {
+  __shared__ uint64_t small[kSmall];
   __shared__ uint32_t csel[kMaxChunks];
   __shared__ uint32_t h256[256];
-  __shared__ uint32_t scan_tmp[kNT / kWave];
-  __shared__ uint32_t bcast[2];
-  __shared__ uint32_t s_last;
+  __shared__ uint32_t tmp[kNT / kWave];
+  __shared__ uint32_t bc[4];
+  __shared__ uint32_t nsmall;
 
-  const int c = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
-  const RowInfo ri = a.info[r];
-  if (ri.mode != kModeTopk) return;
-  const int64_t n_vis = ri.n_vis;
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t n_vis = visible(a, r);
+  if ((int64_t)a.k >= n_vis) return;
   const int64_t nch = chunks_of(n_vis, a.CH);
-  if (c >= nch) return;
+  const uint32_t r1 = a.rowsel[4 * r + 1];
+  const uint32_t* ccnt_row = a.ccnt + (size_t)r * a.C;
+  const uint32_t* cgt_row = a.cgt + (size_t)r * a.C;
+  const uint64_t* cand_row = a.cand + (size_t)r * a.n_cap;
 
-  const uint32_t* keys_row = a.keys + (size_t)r * a.n_cap;
-  uint64_t* cand_row = a.cand + (size_t)r * a.n_cap;
-  const int64_t j0 = (int64_t)c * a.CH;
-  uint32_t gt = 0;
-  for (int it = 0; it < a.CH / kNT; ++it) {
-    const int64_t j = j0 + (int64_t)it * kNT + tid;
-    const bool valid = j < n_vis;
-    const uint32_t key = valid ? keys_row[j] : 0u;
-    const uint32_t bk = key >> kBucketShift;
-    gt += (valid && bk > ri.T1) ? 1u : 0u;
-    const bool isc = valid && bk == ri.T1;
-    const uint64_t mask = __ballot(isc);
-    if (mask) {
-      const int leader = __ffsll((unsigned long long)mask) - 1;
-      uint32_t base = 0;
-      if (lane == leader) base = atomicAdd(&a.ccount[r], (uint32_t)__popcll(mask));
-      base = __shfl(base, leader);
-      if (isc) cand_row[base + lanes_below(mask)] = composite(key, (uint32_t)j);
-    }
-  }
-  const uint32_t tot = wave_sum_u32(gt);
-  if (lane == 0) scan_tmp[w] = tot;
+  // second-level bin T2 of the r1-th largest candidate, and the rank left in it
+  if (tid == 0) nsmall = 0;
+  find_bin_desc<kBuckets>(a.ghist2 + (size_t)r * kBuckets, r1, tmp, bc);
+  const uint32_t T2 = bc[0];
+  const uint32_t r2 = bc[1];
   __syncthreads();
-  if (tid == 0) {
-    uint32_t t = 0;
-    for (int i = 0; i < kNT / kWave; ++i) t += scan_tmp[i];
-    a.cnt[(size_t)r * a.C + c] = t;
-  }
-  __syncthreads();
-  if (tid == 0) s_last = (arrive_release(&a.ticket2[r]) == (uint32_t)(nch - 1)) ? 1u : 0u;
-  __syncthreads();
-  if (!s_last) return;
-  acquire_device();
 
-  // ---- last workgroup of the row: exact select among the candidates ----
-  const uint32_t n_c = load_relaxed(&a.ccount[r]);
-  const uint64_t* src = cand_row;
-  if (n_c <= (uint32_t)kCandLds) {
-    for (uint32_t i = tid; i < n_c; i += kNT) cbuf[i] = cand_row[i];
-    __syncthreads();
-    src = cbuf;
-  }
-  const uint64_t Tc = block_select_desc(src, n_c, ri.r1, h256, scan_tmp, bcast);
-
-  for (int64_t i = tid; i < nch; i += kNT) csel[i] = 0u;
-  __syncthreads();
-  for (uint32_t i = tid; i < n_c; i += kNT) {
-    const uint64_t v = src[i];
-    if (v >= Tc) {
-      const uint32_t j = ~(uint32_t)v;
-      atomicAdd(&csel[j / (uint32_t)a.CH], 1u);
-    }
-  }
-  __syncthreads();
+  // each thread owns whole chunks: count candidates above T2, collect those in T2
   const int per = (int)ceil_div64(nch, kNT);
   const int64_t cs = (int64_t)tid * per;
-  uint32_t loc = 0;
-  for (int i = 0; i < per; ++i)
-    if (cs + i < nch) loc += load_relaxed(&a.cnt[(size_t)r * a.C + cs + i]) + csel[cs + i];
-  const uint32_t incl = block_incl_scan<kNT>(loc, scan_tmp);
-  uint32_t run = incl - loc;
   for (int i = 0; i < per; ++i) {
-    if (cs + i < nch) {
-      a.coff[(size_t)r * a.C + cs + i] = run;
-      run += load_relaxed(&a.cnt[(size_t)r * a.C + cs + i]) + csel[cs + i];
+    const int64_t c = cs + i;
+    if (c >= nch) break;
+    const uint32_t nc = ccnt_row[c];
+    const uint64_t* cp = cand_row + c * a.CH;
+    uint32_t above = 0;
+#pragma unroll 8
+    for (uint32_t e = 0; e < nc; ++e) {
+      const uint64_t v = cp[e];
+      const uint32_t b2 = (uint32_t)(v >> 42) & 2047u;
+      above += b2 > T2 ? 1u : 0u;
+      if (b2 == T2) {
+        const uint32_t slot = atomicAdd(&nsmall, 1u);
+        if (slot < (uint32_t)kSmall) small[slot] = v;
+      }
+    }
+    csel[c] = above;
+  }
+  __syncthreads();
+  const uint32_t m = nsmall;
+  if (m <= (uint32_t)kSmall) {
+    // the r2-th largest of m distinct composites: count the larger ones
+    if (tid < (int)m) {
+      const uint64_t v = small[tid];
+      uint32_t larger = 0;
+      for (uint32_t j = 0; j < m; ++j) larger += small[j] > v ? 1u : 0u;
+      if (larger + 1 == r2) {
+        bc[2] = (uint32_t)v;
+        bc[3] = (uint32_t)(v >> 32);
+      }
+    }
+  } else {
+    // degenerate: too many equal top bits; radix select over the low 42 bits
+    auto visit = [&](auto f) {
+      for (int i = 0; i < per; ++i) {
+        const int64_t c = cs + i;
+        if (c >= nch) break;
+        const uint32_t nc = ccnt_row[c];
+        for (uint32_t e = 0; e < nc; ++e) {
+          const uint64_t v = cand_row[c * a.CH + e];
+          if (((uint32_t)(v >> 42) & 2047u) == T2) f(v & ((1ull << 42) - 1));
+        }
+      }
+    };
+    const uint64_t low = block_select_desc(visit, r2, h256, tmp, bc);
+    if (tid == 0) {
+      const uint64_t v = low | ((uint64_t)T2 << 42);
+      bc[2] = (uint32_t)v;
+      bc[3] = (uint32_t)(v >> 32);
     }
   }
-  if (tid == 0) a.info[r].Tc = Tc;
+  __syncthreads();
+  const uint64_t Tc = ((uint64_t)bc[3] << 32) | bc[2];
+
+  // selected boundary-bin candidates, per chunk
+  if (m <= (uint32_t)kSmall) {
+    for (uint32_t i = tid; i < m; i += kNT)
+      if (small[i] >= Tc) atomicAdd(&csel[(~(uint32_t)small[i]) / (uint32_t)a.CH], 1u);
+  } else {
+    for (int i = 0; i < per; ++i) {
+      const int64_t c = cs + i;
+      if (c >= nch) break;
+      const uint32_t nc = ccnt_row[c];
+      uint32_t add = 0;
+      for (uint32_t e = 0; e < nc; ++e) {
+        const uint64_t v = cand_row[c * a.CH + e];
+        add += (((uint32_t)(v >> 42) & 2047u) == T2 && v >= Tc) ? 1u : 0u;
+      }
+      csel[c] += add;
+    }
+  }
+  __syncthreads();
+
+  // output offset of every chunk: keys above T1 plus selected candidates
+  uint32_t loc = 0;
+  for (int i = 0; i < per; ++i)
+    if (cs + i < nch) loc += cgt_row[cs + i] + csel[cs + i];
+  const uint32_t incl = block_incl_scan<kNT>(loc, tmp);
+  uint32_t run = incl - loc;
+  uint32_t* off_row = a.off + (size_t)r * a.C;
+  for (int i = 0; i < per; ++i) {
+    if (cs + i < nch) {
+      off_row[cs + i] = run;
+      run += cgt_row[cs + i] + csel[cs + i];
+    }
+  }
+  if (tid == 0) {
+    a.rowsel[4 * r + 2] = (uint32_t)Tc;
+    a.rowsel[4 * r + 3] = (uint32_t)(Tc >> 32);
+  }
 }
 
 // ----------------------------------------------------------------- compact
+template <bool TOPK>
 __global__ __launch_bounds__(kNT) void route_compact(RouteArgs a) {
+  __shared__ uint32_t tmp[kNT / kWave];
   __shared__ uint32_t wcnt[kNT / kWave];
+
   const int c = blockIdx.x, r = blockIdx.y;
-  const int tid = threadIdx.x, w = tid / kWave;
-  const RowInfo ri = a.info[r];
-  const int64_t n_vis = ri.n_vis;
+  const int tid = threadIdx.x;
+  const int64_t n_vis = visible(a, r);
   const int64_t nch = chunks_of(n_vis, a.CH);
   if (c >= nch) return;
-
   const uint32_t* keys_row = a.keys + (size_t)r * a.n_cap;
   int32_t* out = a.idx + (size_t)r * a.cap;
   const int64_t j0 = (int64_t)c * a.CH;
-  int64_t run = (ri.mode == kModeAll) ? j0 : (int64_t)a.coff[(size_t)r * a.C + c];
+  const uint32_t* cgt_row = a.cgt + (size_t)r * a.C;
+
+  // mode: 0 all visible keys, 1 top-k rule, 2 threshold rule
+  int mode = 2;
+  uint32_t count = 0, T1 = 0, thr = 0;
+  uint64_t Tc = 0;
+  int64_t run = 0;
+  if (TOPK) {
+    if ((int64_t)a.k >= n_vis) {
+      mode = 0;
+      count = (uint32_t)n_vis;
+      run = j0;
+    } else {
+      mode = 1;
+      count = (uint32_t)a.k;
+      T1 = a.rowsel[4 * r];
+      Tc = ((uint64_t)a.rowsel[4 * r + 3] << 32) | a.rowsel[4 * r + 2];
+      run = a.off[(size_t)r * a.C + c];
+    }
+  } else {
+    thr = score_key(a.tau[r]);
+    count = block_sum_prefix(cgt_row, nch, tmp);  // true set size
+    run = block_sum_prefix(cgt_row, c, tmp);
+  }
 
   for (int it = 0; it < a.CH / kNT; ++it) {
     const int64_t jb = j0 + (int64_t)it * kNT;
     if (jb >= n_vis) break;
     const int64_t j = jb + tid;
     bool p = j < n_vis;
-    if (p && ri.mode != kModeAll) {
+    if (p && mode != 0) {
       const uint32_t key = keys_row[j];
-      if (ri.mode == kModeThresh) {
-        p = key >= ri.T1;
+      if (mode == 2) {
+        p = key >= thr;
       } else {
         const uint32_t bk = key >> kBucketShift;
-        p = bk > ri.T1 || (bk == ri.T1 && composite(key, (uint32_t)j) >= ri.Tc);
+        p = bk > T1 || (bk == T1 && composite(key, (uint32_t)j) >= Tc);
       }
     }
-    const uint64_t mask = __ballot(p);
-    if (lane_id() == 0) wcnt[w] = (uint32_t)__popcll(mask);
-    __syncthreads();
-    uint32_t before = 0, total = 0;
-#pragma unroll
-    for (int i = 0; i < kNT / kWave; ++i) {
-      before += (i < w) ? wcnt[i] : 0u;
-      total += wcnt[i];
-    }
+    uint32_t tot;
+    const uint32_t slot = block_rank(p, wcnt, &tot);
     if (p) {
-      const int64_t o = run + before + lanes_below(mask);
+      const int64_t o = run + slot;
       if (o < a.cap) out[o] = (int32_t)j;
     }
-    run += total;
-    __syncthreads();
+    run += tot;
   }
 
   if (c == 0) {
-    const uint32_t count = ri.count;
     if (tid == 0) a.counts[r] = (int32_t)count;
     const int64_t first = count < (uint32_t)a.cap ? (int64_t)count : (int64_t)a.cap;
     for (int64_t i = first + tid; i < a.cap; i += kNT) out[i] = -1;
@@ -477,7 +580,7 @@ __global__ __launch_bounds__(kNT) void route_compact(RouteArgs a) {
 // ------------------------------------------------------------------- host
 struct Layout {
   int CH, C;
-  size_t o_t1, o_t2, o_cc, o_gh, ctrl_end, o_info, o_cnt, o_coff, o_keys, o_cand, total;
+  size_t o_gh, o_gh2, ctrl_end, o_rowsel, o_cgt, o_ccnt, o_off, o_keys, o_cand, total;
 };
 
 Layout make_layout(int64_t R, int64_t n_cap, bool topk) {
@@ -487,15 +590,15 @@ Layout make_layout(int64_t R, int64_t n_cap, bool topk) {
   L.CH = (int)CH;
   L.C = (int)ceil_div64(n_cap, CH);
   size_t o = 0;
-  L.o_t1 = o; o += (size_t)R * 4;
-  L.o_t2 = o; o += topk ? (size_t)R * 4 : 0;
-  L.o_cc = o; o += topk ? (size_t)R * 4 : 0;
-  L.o_gh = o; o += topk ? (size_t)R * kBuckets * 4 : 0;
-  o = align_up(o, 256);
+  L.o_gh = o;
+  o = align_up(o + (topk ? (size_t)R * kBuckets * 4 : 0), 256);
+  L.o_gh2 = o;
+  o = align_up(o + (topk ? (size_t)R * kBuckets * 4 : 0), 256);
   L.ctrl_end = o;
-  L.o_info = o; o = align_up(o + (size_t)R * sizeof(RowInfo), 256);
-  L.o_cnt = o; o = align_up(o + (size_t)R * L.C * 4, 256);
-  L.o_coff = o; o = align_up(o + (size_t)R * L.C * 4, 256);
+  L.o_rowsel = o; o = align_up(o + (size_t)R * 16, 256);
+  L.o_cgt = o; o = align_up(o + (size_t)R * L.C * 4, 256);
+  L.o_ccnt = o; o = align_up(o + (topk ? (size_t)R * L.C * 4 : 0), 256);
+  L.o_off = o; o = align_up(o + (topk ? (size_t)R * L.C * 4 : 0), 256);
   L.o_keys = o; o = align_up(o + (size_t)R * n_cap * 4, 256);
   L.o_cand = o; o = align_up(o + (topk ? (size_t)R * n_cap * 8 : 0), 256);
   L.total = o;
@@ -511,16 +614,16 @@ bool shape_ok(int B, int M, int d, int64_t n_cap, int cap) {
   return true;
 }
 
-template <uint32_t MODE>
+template <bool TOPK>
 void launch_score(const RouteArgs& a, clsa_dtype dt, int d, dim3 grid, hipStream_t s) {
   if (dt == CLSA_BF16) {
-    if (d == 32) hipLaunchKernelGGL((route_score<uint16_t, 32, MODE>), grid, dim3(kNT), 0, s, a);
-    if (d == 64) hipLaunchKernelGGL((route_score<uint16_t, 64, MODE>), grid, dim3(kNT), 0, s, a);
-    if (d == 128) hipLaunchKernelGGL((route_score<uint16_t, 128, MODE>), grid, dim3(kNT), 0, s, a);
+    if (d == 32) hipLaunchKernelGGL((route_score<uint16_t, 32, TOPK>), grid, dim3(kNT), 0, s, a);
+    if (d == 64) hipLaunchKernelGGL((route_score<uint16_t, 64, TOPK>), grid, dim3(kNT), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((route_score<uint16_t, 128, TOPK>), grid, dim3(kNT), 0, s, a);
   } else {
-    if (d == 32) hipLaunchKernelGGL((route_score<float, 32, MODE>), grid, dim3(kNT), 0, s, a);
-    if (d == 64) hipLaunchKernelGGL((route_score<float, 64, MODE>), grid, dim3(kNT), 0, s, a);
-    if (d == 128) hipLaunchKernelGGL((route_score<float, 128, MODE>), grid, dim3(kNT), 0, s, a);
+    if (d == 32) hipLaunchKernelGGL((route_score<float, 32, TOPK>), grid, dim3(kNT), 0, s, a);
+    if (d == 64) hipLaunchKernelGGL((route_score<float, 64, TOPK>), grid, dim3(kNT), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((route_score<float, 128, TOPK>), grid, dim3(kNT), 0, s, a);
   }
 }
 
@@ -543,13 +646,12 @@ RouteArgs fill_args(const Layout& L, void* ws, const void* q_idx, const void* K_
   a.cap = cap;
   a.CH = L.CH;
   a.C = L.C;
-  a.ticket1 = reinterpret_cast<uint32_t*>(base + L.o_t1);
-  a.ticket2 = reinterpret_cast<uint32_t*>(base + L.o_t2);
-  a.ccount = reinterpret_cast<uint32_t*>(base + L.o_cc);
   a.ghist = reinterpret_cast<uint32_t*>(base + L.o_gh);
-  a.info = reinterpret_cast<RowInfo*>(base + L.o_info);
-  a.cnt = reinterpret_cast<uint32_t*>(base + L.o_cnt);
-  a.coff = reinterpret_cast<uint32_t*>(base + L.o_coff);
+  a.ghist2 = reinterpret_cast<uint32_t*>(base + L.o_gh2);
+  a.rowsel = reinterpret_cast<uint32_t*>(base + L.o_rowsel);
+  a.cgt = reinterpret_cast<uint32_t*>(base + L.o_cgt);
+  a.ccnt = reinterpret_cast<uint32_t*>(base + L.o_ccnt);
+  a.off = reinterpret_cast<uint32_t*>(base + L.o_off);
   a.keys = reinterpret_cast<uint32_t*>(base + L.o_keys);
   a.cand = reinterpret_cast<uint64_t*>(base + L.o_cand);
   return a;
@@ -582,9 +684,10 @@ extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, in
                                 idx, counts, cap);
   if (zero_fill(ws, L.ctrl_end, s) != hipSuccess) return CLSA_ERR_HIP;
   const dim3 grid((unsigned)L.C, (unsigned)R);
-  launch_score<kModeTopk>(a, dt, d, grid, s);
+  launch_score<true>(a, dt, d, grid, s);
   hipLaunchKernelGGL(route_cands, grid, dim3(kNT), 0, s, a);
-  hipLaunchKernelGGL(route_compact, grid, dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(route_select, dim3((unsigned)R), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(route_compact<true>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
 }
 
@@ -609,9 +712,8 @@ extern "C" int clsa_route_threshold(const void* q_idx, const void* K_idx, int B,
   hipStream_t s = static_cast<hipStream_t>(stream);
   const RouteArgs a = fill_args(L, ws, q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, 1, tau, idx,
                                 counts, cap);
-  if (zero_fill(ws, L.ctrl_end, s) != hipSuccess) return CLSA_ERR_HIP;
   const dim3 grid((unsigned)L.C, (unsigned)R);
-  launch_score<kModeThresh>(a, dt, d, grid, s);
-  hipLaunchKernelGGL(route_compact, grid, dim3(kNT), 0, s, a);
+  launch_score<false>(a, dt, d, grid, s);
+  hipLaunchKernelGGL(route_compact<false>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
 }

@@ -68,9 +68,12 @@ def test_route_workspace_sizes(lib):
 
 
 def test_attn_workspace_sizes(lib):
-    # split lists need partials; one long row per layer needs none
-    assert lib.clsa_sparse_attn_workspace_size(16, 8, 1, 32, 8, 128, 2048, BF16) > 0
+    # one sequence is too few workgroups: its lists are split and need
+    # partials; 8 sequences x 8 KV heads x 16 layers fill the chip unsplit
+    assert lib.clsa_sparse_attn_workspace_size(16, 1, 1, 32, 8, 128, 2048, BF16) > 0
+    assert lib.clsa_sparse_attn_workspace_size(16, 8, 1, 32, 8, 128, 2048, BF16) == 0
     assert lib.clsa_sparse_attn_workspace_size(16, 1, 4096, 32, 8, 128, 2048, BF16) == 0
+    assert lib.clsa_sparse_attn_workspace_size(1, 1, 1, 4, 2, 64, 300, F32) > 0  # VALU path
     assert lib.clsa_sparse_attn_workspace_size(16, 8, 1, 30, 8, 128, 2048, BF16) == 0  # Hq%Hkv
 
 
@@ -119,6 +122,19 @@ def _attn(lib, L=2, B=1, M=1, Hq=32, Hkv=8, D=128, cap=2048, scale=0.0, dt=BF16,
 ])
 def test_attn_rejects(lib, kw, want):
     assert _attn(lib, **kw) == want
+
+
+def test_kv_append_rejects(lib):
+    arr = ctypes.c_void_p * 2
+    a = arr(0x100000, 0x100000)
+    f = lib.clsa_kv_append
+    assert f(2, 8, 8, 128, 64, 4096, NULL, FAKE, FAKE, a, a, a, a, BF16, NULL) == INVALID  # pos
+    assert f(2, 8, 8, 128, 64, 4096, FAKE, FAKE, NULL, a, a, a, a, BF16, NULL) == INVALID
+    assert f(2, 8, 8, 128, 12, 4096, FAKE, FAKE, FAKE, a, a, a, a, BF16, NULL) == INVALID  # d
+    assert f(65, 8, 8, 128, 64, 4096, FAKE, FAKE, FAKE, a, a, a, a, BF16, NULL) == INVALID
+    assert f(2, 8, 8, 128, 64, 4096, FAKE, FAKE, FAKE, a, a, a, a, 9, NULL) == DTYPE
+    bad = arr(0x100000, 0)
+    assert f(2, 8, 8, 128, 64, 4096, FAKE, FAKE, FAKE, a, bad, a, a, BF16, NULL) == INVALID
 
 
 def test_binding_fails_loudly_without_library(tmp_path):

@@ -100,6 +100,26 @@ def test_route_zero_query_takes_lowest_positions():
         assert np.all(gi[b, 0, 100:] == -1)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_route_degenerate_bucket_uses_global_select(dtype):
+    # every score lies in one histogram bucket ([2, 2.5)), with only 64 distinct
+    # bf16 values: more candidates than the LDS select holds, and exact ties
+    g = _cpu_gen(17)
+    B, N = 2, 20000
+    K = torch.zeros((B, N, 32))
+    K[:, :, 0] = 2.0 + 0.49 * torch.rand((B, N), generator=g)
+    K[:, :, 1:] = 0.01 * torch.randn((B, N, 31), generator=g)
+    K = K.to(torch.bfloat16).to(dtype)
+    q = torch.zeros((B, 1, 32), dtype=dtype)
+    q[:, 0, 0] = 1.0
+    for k in (1, 2048, 9999):
+        idx, counts = clsa.route(q.to(DEV), K.to(DEV), k)
+        assert _check_route(idx, counts, q, K, [N, N], -1, k, k) == 0  # exact scores
+    q0 = torch.zeros((B, 1, 32), dtype=dtype)  # all scores exactly 0
+    idx, counts = clsa.route(q0.to(DEV), K.to(DEV), 7000)
+    assert idx.cpu()[:, 0].tolist() == [list(range(7000))] * B
+
+
 def test_route_prefill_causal_rows():
     g = _cpu_gen(13)
     K = torch.randn((2, 3000, 64), generator=g).to(torch.bfloat16)
@@ -217,8 +237,8 @@ def test_attn_fp32_generic():
 
 
 @pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 8, 128), (16, 8, 64), (32, 4, 128),
-                                      (64, 4, 64), (16, 1, 128)])
-def test_attn_bf16_mfma_shapes(Hq, Hkv, D):
+                                      (64, 4, 64), (16, 1, 128), (16, 2, 256), (8, 8, 256)])
+def test_attn_bf16_fast_shapes(Hq, Hkv, D):
     case = _attn_case(torch.bfloat16, 2, 2, 2, Hq, Hkv, D, 5000, 700, [0, 1, 700, 65], 22 + Hq)
     _check_attn(*case)
 
@@ -422,3 +442,23 @@ def test_workload_threshold_128k_b16():
     _attn_full_launch_vs_oracle(q, Kc, Vc, idx, out, o_lists, [0, 15], cap)
     del Kc, Vc, q, out, K_idx
     _free()
+
+
+def test_kv_append_writes_each_sequence_slot():
+    g = _cpu_gen(31)
+    L, B, n_cap, Hkv, D, d = 3, 4, 50, 8, 128, 64
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
+    Ki = torch.randn((B, n_cap, d), generator=g).to(torch.bfloat16).to(DEV)
+    nk = torch.randn((L, B, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
+    nv = torch.randn((L, B, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
+    ni = torch.randn((B, d), generator=g).to(torch.bfloat16).to(DEV)
+    pos = torch.tensor([0, 17, 49, 50], dtype=torch.int32, device=DEV)  # 50: out of range
+    K0, V0, Ki0 = K.clone(), V.clone(), Ki.clone()
+    clsa.kv_append(pos, ni, Ki, nk, K, nv, V)
+    torch.cuda.synchronize()
+    for b, p in enumerate([0, 17, 49]):
+        K0[:, b, p] = nk[:, b]
+        V0[:, b, p] = nv[:, b]
+        Ki0[b, p] = ni[b]
+    assert torch.equal(K, K0) and torch.equal(V, V0) and torch.equal(Ki, Ki0)
