@@ -23,6 +23,31 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+ATTN_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_decode_128k_b8.md")
+ATTN_SOURCES = ["long_context_sparse_routing_amd/csrc/clsa_attn.hip",
+                "long_context_sparse_routing_amd/csrc/clsa_common.h"]
+
+
+def profiled_traffic():
+    """HBM bytes per attention launch measured with rocprofv3 (FETCH_SIZE and
+    WRITE_SIZE, calibrated on a plain copy) as recorded in the committed
+    profile summary -- or None when the kernel sources changed since."""
+    import hashlib
+    try:
+        text = open(ATTN_PROFILE).read()
+    except OSError:
+        return None
+    m = hashlib.sha256()
+    for p in ATTN_SOURCES:
+        m.update(open(os.path.join(ROOT, p), "rb").read())
+    digest = m.hexdigest()[:16]
+    if f": {digest}" not in text:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            return float(line.split(":")[1])
+    return None
 
 
 def attn_bytes(L, B, M, Hq, Hkv, D, k, esize=2):
@@ -96,6 +121,8 @@ def main():
     ap.add_argument("--workload", default="decode_128k_b8")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work in the baseline sample (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
@@ -109,6 +136,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 2,
+                          "copy_calibration_bytes_written": dst.numel() * 2, "launches": 5}))
+        return
     clsa.load_library()
     base = gen.WORKLOADS[args.workload]
     total_steps = args.warmup + args.steps
@@ -209,9 +245,10 @@ def main():
         "step_breakdown_ms": {"route_call": route_ms, "attn_call": attn_ms,
                               "append_and_gaps": ms_step - route_ms - attn_ms,
                               "route_call_source": "separate pass after the timed loop"},
-        "roofline": {"kernel": "attn_mfma<4,128> (clsa_sparse_attn call, 16 layers)",
+        "roofline": {"kernel": "attn_bf16<4,128> (one clsa_sparse_attn launch, 16 layers)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": profiled_traffic(),
                      "algorithmic_bytes_per_launch": a_bytes},
         "route_roofline": {"achieved": r_bytes / (route_ms * 1e-3) / 1e9, "unit": "GB/s",
                            "frac": r_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
