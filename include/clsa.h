@@ -88,6 +88,14 @@ const char* clsa_status_string(int status);
  * products (bf16 x bf16 is exact in fp32).  Selection: the counts largest
  * scores; equal scores are taken in increasing j.  -0.0 equals +0.0.
  * d must be 32, 64 or 128.
+ * Blocks of query rows (bf16, M >= 64, k <= 2048, n_cap <= 512K, e.g. a
+ * prefill chunk) score on the matrix cores: the score matrix is filtered
+ * against a per-row sampled threshold inside the MFMA epilogue and never
+ * written out; the workspace then holds up to 8 bytes per (row, key) for
+ * the filtered candidates.  Scores within a row are computed one way for
+ * every key, so the selection and tie rule are the same on both paths; the
+ * scores themselves may differ from the one-query path in the last bits
+ * (fp32 summation order).
  * Errors: CLSA_ERR_INVALID (null pointer, B/M/k < 1, d unsupported,
  * n_cap < 1, cap < k, B*M*n_cap too large), CLSA_ERR_UNSUPPORTED_DTYPE,
  * CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libclsa.so")
-SOURCES = ["clsa_api.hip", "clsa_route.hip", "clsa_attn.hip"]
+SOURCES = ["clsa_api.hip", "clsa_route.hip", "clsa_prefill.hip", "clsa_attn.hip"]
 ARCH = os.environ.get("CLSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -31,9 +31,14 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  The block-routing kernels consume MFMA results
+# with VALU compares; results in AGPRs would cost a v_accvgpr_read per value.
+EXTRA = {"clsa_prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{res.stderr}")

@@ -95,6 +95,27 @@ CLSA_DEV uint32_t block_incl_scan(uint32_t v, uint32_t* tmp) {
   return inc + add;
 }
 
+// Ordered compaction of one NT-element slice: returns this thread's slot
+// among the set predicates of the slice (ascending thread order) and the
+// slice's total in *total.  `wcnt` holds one uint32 per wave; every thread
+// of the block must call it.
+template <int NT = 256>
+CLSA_DEV uint32_t block_rank(bool p, uint32_t* wcnt, uint32_t* total) {
+  const int w = threadIdx.x / kWave;
+  const uint64_t mask = __ballot(p);
+  if (lane_id() == 0) wcnt[w] = (uint32_t)__popcll(mask);
+  __syncthreads();
+  uint32_t before = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    before += (i < w) ? wcnt[i] : 0u;
+    tot += wcnt[i];
+  }
+  __syncthreads();
+  *total = tot;
+  return before + lanes_below(mask);
+}
+
 // ------------------------------------------------------------ memory order
 // Release this workgroup's prior global writes to the whole device, then
 // count one arrival on `ticket`; returns the previous count.

@@ -1,0 +1,946 @@
+// Block routing: top-k for many query rows of one sequence (a prefill chunk),
+// with the score matrix on the matrix cores.
+//
+// Method: CLSA explainer (ai-papers.net), section "CLSAの仕組み" -- the
+// self-decoder picks the top-k KV positions of every query token once; for a
+// chunk of M query tokens that is the dense score matrix Q_idx K_idx^T
+// (causally masked) followed by a row-wise top-k.  The scores are a real
+// dense contraction, so they run on v_mfma_f32_32x32x16_bf16 and the score
+// matrix never reaches HBM.
+//
+//   block_sample   scores of every row against every kSStride-th key (MFMA),
+//                  stored as order-preserving keys.
+//   block_thresh   per row, the rho-th largest sampled score (exact radix
+//                  select), rho chosen so that, with a four-sigma margin,
+//                  at least k keys of the row score that much.  It becomes
+//                  the row's filter threshold T.
+//   block_filter   the full score matrix in 32x32 MFMA tiles, keys as the A
+//                  operand and queries as B, so each lane owns one query
+//                  column; keys scoring >= T are appended as (score,
+//                  position) to a segment of the lane's own, through a small
+//                  LDS ring: no atomics, no cross-lane work per hit.
+//   block_select   per row: the exact top-k among the candidates (lower
+//                  positions win ties), written in ascending order.  A row
+//                  whose threshold kept fewer than k keys, or more than the
+//                  select holds, is redone by an exact rescan (rare).
+// All keys of a row are ranked on values computed the same way, so equal key
+// rows score exactly equal and the lower position wins.
+#include "clsa_common.h"
+
+namespace clsa {
+namespace {
+
+constexpr int kNT = 256;           // threads of the sample/thresh/select kernels
+constexpr int kFT = 256;           // threads of the filter kernel (4 waves)
+constexpr int kSStride = 32;       // sampling stride of the threshold estimate
+constexpr int kSampRows = 256;     // rows per sample workgroup (4 waves x 64)
+constexpr int kFiltRows = 256;     // rows per filter workgroup (4 waves x 64)
+constexpr int kChunk = 1024;       // keys per filter workgroup
+constexpr int kHalf = kChunk / 2;  // keys one half-wave scores per chunk
+constexpr int kStageKeys = 64;     // keys staged in LDS per step
+constexpr int kSelCap = 6144;      // candidates a select workgroup holds
+constexpr int kMaxK = 2048;
+constexpr int kMaxChunks = 512;    // key chunks per row
+constexpr int kThrLds = 8192;      // sampled keys the thresh kernel holds
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct BlockArgs {
+  const uint16_t* q;       // [B][M][d] bf16
+  const uint16_t* K;       // [B][n_cap][d] bf16
+  const int32_t* n_ctx;    // [B] or null
+  int32_t* idx;            // [B][M][cap]
+  int32_t* counts;         // [B][M]
+  int64_t n_cap, q_pos0;
+  int B, M, k, cap;
+  int ns_max;              // sampled keys per row (max)
+  int nchunks;             // key chunks per row
+  uint32_t* samp;          // [R][ns_max] sampled score keys
+  float* thr;              // [R] filter threshold; -inf: every key, +inf: none
+  uint32_t* segcnt;        // [R][nchunks][2] candidates per half-segment
+  uint64_t* seg;           // [R][nchunks][2][kHalf]: position | score << 32
+};
+
+CLSA_DEV int64_t row_visible(const BlockArgs& a, int b, int m) {
+  int64_t n = a.n_ctx ? (int64_t)a.n_ctx[b] : a.n_cap;
+  n = n < 0 ? 0 : (n > a.n_cap ? a.n_cap : n);
+  if (a.q_pos0 >= 0) {
+    const int64_t lim = a.q_pos0 + m + 1;
+    n = n < lim ? n : lim;
+  }
+  return n;
+}
+
+// Operands of a 32-row slab for v_mfma_f32_32x32x16_bf16: lane l holds row
+// l%32, dims 16*st + 8*(l/32) .. +7 for k-step st (A and B layouts agree).
+template <int D>
+CLSA_DEV void load_q_slab(const BlockArgs& a, int b, int m0, bf16x8_t (&qa)[D / 16]) {
+  const int lane = lane_id();
+  const int m = m0 + lane % 32;
+  const bool ok = m < a.M;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st) {
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (ok)
+      v = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)b * a.M + m) * D + st * 16 +
+                                              8 * (lane / 32));
+    qa[st] = __builtin_bit_cast(bf16x8_t, v);
+  }
+}
+
+// Staged keys in LDS: key n holds D/8 16-byte pieces; piece c sits in slot
+// c ^ (n % (D/8)), so 32 lanes reading one piece of 32 keys spread over the
+// banks.
+template <int D>
+CLSA_DEV int lds_piece(int n, int c) {
+  constexpr int P = D / 8;
+  return n * P + (c ^ (n & (P - 1)));
+}
+
+// keys key0 + n*stride (n < kStageKeys) into LDS, zeros at positions >= n_lim
+template <int D, int NT>
+CLSA_DEV void stage_keys(const BlockArgs& a, int b, int64_t key0, int64_t stride, int64_t n_lim,
+                         u32x4_t* lds) {
+  constexpr int P = D / 8;
+  for (int i = threadIdx.x; i < kStageKeys * P; i += NT) {
+    const int n = i / P, c = i % P;
+    const int64_t j = key0 + (int64_t)n * stride;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (j < n_lim) v = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + c * 8);
+    lds[lds_piece<D>(n, c)] = v;
+  }
+}
+
+template <int D>
+CLSA_DEV void load_k_tile(const u32x4_t* lds, int t, bf16x8_t (&kb)[D / 16]) {
+  const int lane = lane_id();
+  const int n = t * 32 + lane % 32;
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    kb[st] = __builtin_bit_cast(bf16x8_t, lds[lds_piece<D>(n, 2 * st + lane / 32)]);
+}
+
+// c + X Y^T over one 32x32 tile (rows of X against rows of Y)
+template <int D>
+CLSA_DEV f32x16_t tile_mma(const bf16x8_t (&x)[D / 16], const bf16x8_t (&y)[D / 16], f32x16_t c) {
+#pragma unroll
+  for (int st = 0; st < D / 16; ++st)
+    c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[st], y[st], c, 0, 0, 0);
+  return c;
+}
+
+// row of accumulator value v held by lane l (its column is l % 32)
+CLSA_DEV int acc_row(int v, int lane) { return 8 * (v / 4) + 4 * (lane / 32) + (v % 4); }
+
+// ------------------------------------------------------------------ sample
+// grid: (ceil(ns_max / kStageKeys), ceil(M / kSampRows), B)
+template <int D>
+__global__ __launch_bounds__(kNT) void block_sample(BlockArgs a) {
+  __shared__ u32x4_t kst[kStageKeys * D / 8];
+  const int sc = blockIdx.x, rb = blockIdx.y, b = blockIdx.z;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int64_t s0 = (int64_t)sc * kStageKeys;
+  stage_keys<D, kNT>(a, b, s0 * kSStride, kSStride, a.n_cap, kst);
+  __syncthreads();
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int m0 = rb * kSampRows + w * 64 + blk * 32;
+    if (m0 >= a.M) break;
+    bf16x8_t qa[D / 16];
+    load_q_slab<D>(a, b, m0, qa);
+#pragma unroll
+    for (int t = 0; t < kStageKeys / 32; ++t) {
+      bf16x8_t kb[D / 16];
+      load_k_tile<D>(kst, t, kb);
+      const f32x16_t c = tile_mma<D>(qa, kb, f32x16_t{});  // rows: queries, columns: samples
+      const int64_t s = s0 + t * 32 + lane % 32;
+      const int64_t j = s * kSStride;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + acc_row(v, lane);
+        if (m < a.M && s < a.ns_max) {
+          const bool vis = j < row_visible(a, b, m);
+          a.samp[((size_t)b * a.M + m) * a.ns_max + s] = vis ? score_key(c[v]) : 0u;
+        }
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------- LDS radix helpers
+// Bin holding the rank-th largest element of histogram h[0..NB) (bin NB-1
+// holds the largest values); rank is 1-based.  out2 = {bin, rank within}.
+template <int NB>
+CLSA_DEV void find_bin_desc(const uint32_t* h, uint32_t rank, uint32_t* tmp, uint32_t* out2) {
+  constexpr int PER = NB / kNT;
+  const int tid = threadIdx.x;
+  uint32_t v[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    v[i] = h[NB - 1 - PER * tid - i];
+    sum += v[i];
+  }
+  const uint32_t incl = block_incl_scan<kNT>(sum, tmp);
+  const uint32_t excl = incl - sum;
+  if (excl < rank && rank <= incl) {
+    uint32_t acc = excl;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (acc + v[i] >= rank) {
+        out2[0] = (uint32_t)(NB - 1 - PER * tid - i);
+        out2[1] = rank - acc;
+        break;
+      }
+      acc += v[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Exact rank-th largest of the n 32-bit keys get(0 .. n-1), 1 <= rank <= n,
+// by three histogram passes over bits 31..21, 20..10 and 9..0.  *left gets
+// how many elements equal to the result are needed to reach the rank.
+template <class Get>
+CLSA_DEV uint32_t select_key_desc(Get get, uint32_t n, uint32_t rank, uint32_t* h, uint32_t* tmp,
+                                  uint32_t* bc, uint32_t* left) {
+  uint32_t prefix = 0;
+#pragma unroll
+  for (int p = 0; p < 3; ++p) {
+    const int shift = p == 0 ? 21 : (p == 1 ? 10 : 0);
+    const uint32_t width = p == 2 ? 1023u : 2047u;
+    const uint32_t pmask = p == 0 ? 0u : (p == 1 ? 0xFFE00000u : 0xFFFFFC00u);
+    for (int i = threadIdx.x; i < 2048; i += kNT) h[i] = 0u;
+    __syncthreads();
+    for (uint32_t i = threadIdx.x; i < n; i += kNT) {
+      const uint32_t key = get(i);
+      if ((key & pmask) == prefix) atomicAdd(&h[(key >> shift) & width], 1u);
+    }
+    __syncthreads();
+    if (p < 2) find_bin_desc<2048>(h, rank, tmp, bc);
+    else find_bin_desc<1024>(h, rank, tmp, bc);
+    prefix |= bc[0] << shift;
+    rank = bc[1];
+    __syncthreads();
+  }
+  *left = rank;
+  return prefix;
+}
+
+constexpr int kSmall = 256;  // boundary-bin elements ranked pairwise
+
+struct SelScratch {  // LDS scratch of select_kth_desc
+  uint32_t h[2048];
+  uint32_t small[kSmall];
+  uint32_t tmp[kNT / kWave];
+  uint32_t lo[kNT / kWave], hi[kNT / kWave];
+  uint32_t bc[8];
+};
+
+// Exact rank-th largest of the n keys get(0 .. n-1), 1 <= rank <= n; *left
+// gets how many elements equal to it are needed to reach the rank.  One
+// histogram pass over 2048 bins spanning the keys' actual range [lo, hi]
+// (so a narrow range still spreads out), then the boundary bin's elements
+// are ranked pairwise.  A boundary bin above kSmall elements (massive ties)
+// falls back to the full three-pass radix select.
+template <class Get>
+CLSA_DEV uint32_t select_kth_desc(Get get, uint32_t n, uint32_t rank, SelScratch& S,
+                                  uint32_t* left) {
+  const int tid = threadIdx.x, w = tid / kWave;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (uint32_t i = tid; i < n; i += kNT) {
+    const uint32_t k = get(i);
+    lo = k < lo ? k : lo;
+    hi = k > hi ? k : hi;
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t l2 = __shfl_xor(lo, m), h2 = __shfl_xor(hi, m);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
+  }
+  if (lane_id() == 0) S.lo[w] = lo, S.hi[w] = hi;
+  for (int i = tid; i < 2048; i += kNT) S.h[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kNT / kWave; ++i) {
+    lo = S.lo[i] < lo ? S.lo[i] : lo;
+    hi = S.hi[i] > hi ? S.hi[i] : hi;
+  }
+  const uint32_t range = hi - lo;
+  const int shift = range < 2048u ? 0 : (32 - __clz(range)) - 11;
+  for (uint32_t i = tid; i < n; i += kNT) atomicAdd(&S.h[(get(i) - lo) >> shift], 1u);
+  __syncthreads();
+  find_bin_desc<2048>(S.h, rank, S.tmp, S.bc);
+  const uint32_t bin = S.bc[0], r1 = S.bc[1], c1 = S.h[bin];
+  if (c1 > (uint32_t)kSmall) {
+    __syncthreads();
+    return select_key_desc(get, n, rank, S.h, S.tmp, S.bc, left);
+  }
+  if (tid == 0) S.bc[2] = 0u;
+  __syncthreads();
+  for (uint32_t i = tid; i < n; i += kNT) {
+    const uint32_t k = get(i);
+    if (((k - lo) >> shift) == bin) S.small[atomicAdd(&S.bc[2], 1u)] = k;
+  }
+  __syncthreads();
+  for (uint32_t e = tid; e < c1; e += kNT) {
+    const uint32_t v = S.small[e];
+    uint32_t gt = 0, eq = 0;
+    for (uint32_t f = 0; f < c1; ++f) {
+      gt += S.small[f] > v ? 1u : 0u;
+      eq += S.small[f] == v ? 1u : 0u;
+    }
+    if (gt < r1 && r1 <= gt + eq) {  // equal elements all write the same values
+      S.bc[3] = v;
+      S.bc[4] = r1 - gt;
+    }
+  }
+  __syncthreads();
+  const uint32_t kth = S.bc[3];
+  *left = S.bc[4];
+  __syncthreads();
+  return kth;
+}
+
+// inverse of score_key
+CLSA_DEV float key_to_float(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// ------------------------------------------------------------------ thresh
+// one workgroup per row
+__global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
+  __shared__ uint32_t ks[kThrLds];
+  __shared__ SelScratch S;
+  const int r = blockIdx.x;
+  const int b = r / a.M, m = r % a.M;
+  const int64_t n_vis = row_visible(a, b, m);
+  const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
+  if (k_eff >= n_vis) {  // every visible key is selected: no candidates needed
+    if (threadIdx.x == 0) a.thr[r] = INFINITY;
+    return;
+  }
+  const int64_t ns = (n_vis + kSStride - 1) / kSStride;
+  // smallest rho with rho - 4 sqrt(rho) >= k_eff * ns / n_vis
+  const float kappa = (float)k_eff * (float)ns / (float)n_vis;
+  const float sr = 2.0f + sqrtf(4.0f + kappa);
+  const int64_t rho = (int64_t)ceilf(sr * sr);
+  if (rho > ns) {  // too few samples to bound the k-th score: keep every key
+    if (threadIdx.x == 0) a.thr[r] = -INFINITY;
+    return;
+  }
+  const uint32_t* srow = a.samp + (size_t)r * a.ns_max;
+  const bool in_lds = ns <= kThrLds;
+  if (in_lds) {  // eight independent loads in flight per thread
+    for (int64_t i0 = 0; i0 < ns; i0 += 8 * kNT) {
+      uint32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * kNT + threadIdx.x;
+        v[u] = i < ns ? srow[i] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int64_t i = i0 + u * kNT + threadIdx.x;
+        if (i < ns) ks[i] = v[u];
+      }
+    }
+    __syncthreads();
+  }
+  uint32_t left;
+  const uint32_t key = select_kth_desc([&](uint32_t i) { return in_lds ? ks[i] : srow[i]; },
+                                       (uint32_t)ns, (uint32_t)rho, S, &left);
+  if (threadIdx.x == 0) a.thr[r] = key_to_float(key);
+}
+
+// ------------------------------------------------------------------ filter
+// Each workgroup scores kFiltRows query rows against one chunk of kChunk
+// keys, staged through LDS kStageKeys at a time (the next stage's keys are
+// loaded into registers while the current one is scored).
+//
+// A fifth MFMA k-step against a constant column subtracts the row's
+// threshold inside the accumulator: dd = score - T', with T' the threshold
+// rounded down to bf16 (still a lower bound, so nothing is lost).  The sign
+// bits of a stage's 32 values per lane then pack into one hit mask with one
+// v_alignbit each; lanes with hits spill their 32 values to LDS scratch and
+// a loop over set bits, all lanes in parallel, appends (dd, position) to the
+// lane's segment in HBM.  Rows that keep every key (threshold -inf) and
+// tiles crossing a row's visibility limit take explicit compares instead.
+constexpr int kScrStride = 36;  // scratch words per lane (32 values, padded
+                                // so 16 consecutive lanes hit distinct banks)
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() would also wait
+// for every outstanding global load, which defeats the key prefetch; the
+// "memory" clobber keeps the compiler from moving LDS accesses across it.
+CLSA_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// bf16 bits of -x, with x first rounded down to bf16 (toward -inf)
+CLSA_DEV uint16_t neg_bf16_floor(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (x == 0.f) return 0;  // +0: keeps dd = +0 for a zero score
+  const uint32_t t = u & 0xffff0000u;
+  u = (t != u && (u >> 31)) ? t + 0x10000u : t;  // negative: away from zero
+  return (uint16_t)((u ^ 0x80000000u) >> 16);
+}
+
+// Keys [key0, key0 + kStageKeys) as 16-byte pieces, kFT threads: piece
+// i = threadIdx.x + u*kFT is key i / (D/8), dims 8*(i % (D/8)) ..; keys at or
+// beyond key_hi read as zeros.
+template <int D>
+struct StageRegs {
+  static constexpr int kPieces = kStageKeys * D / 8;
+  static constexpr int kPer = (kPieces + kFT - 1) / kFT;
+  u32x4_t v[kPer];
+
+  CLSA_DEV void load(const BlockArgs& a, int b, int64_t key0, int64_t key_hi) {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + u * kFT;
+      const int64_t j = key0 + i / (D / 8);
+      v[u] = u32x4_t{0u, 0u, 0u, 0u};
+      if (i < kPieces && j < key_hi)
+        v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % (D / 8)) * 8);
+    }
+  }
+  CLSA_DEV void store(u32x4_t* lds) const {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = threadIdx.x + u * kFT;
+      if (i < kPieces) lds[lds_piece<D>(i / (D / 8), i % (D / 8))] = v[u];
+    }
+  }
+};
+
+struct SlabState {
+  bf16x8_t tq;      // k-step operand: -T' in dim 0 (lanes < 32)
+  float lo;         // 0, or -inf when the row keeps every key
+  int32_t lim;      // keys visible to the lane's row
+  int32_t lim_min;  // min over the slab (wave-uniform)
+  bool sign_ok;     // every row of the slab has a finite threshold (uniform)
+  uint64_t* segp;   // the lane's half-segment in HBM
+  uint32_t gcnt;    // entries written there
+};
+
+// One stage (two 32-key tiles) of one slab: the 32 values of this lane's
+// query, value i being key jl0 + 2*(i & 28) + (i & 3).  Returns the hit
+// mask, bit i for value i.
+template <bool CHECK>
+CLSA_DEV uint32_t stage_hits(const f32x16_t& x0, const f32x16_t& x1, const SlabState& st,
+                             int32_t jl0) {
+  uint32_t m = 0;  // after the chain, bit i is the sign of value i (1: miss)
+  // opaque copy: keeps the compiler from hoisting the compare path's
+  // position arithmetic into the fast path
+  if (CHECK) asm volatile("" : "+v"(jl0));
+#pragma unroll
+  for (int i = 31; i >= 0; --i) {
+    const float x = i < 16 ? x0[i] : x1[i - 16];
+    if (CHECK) {
+      const int32_t j = jl0 + 2 * (i & 28) + (i & 3);
+      const bool hit = x >= st.lo && j < st.lim;
+      m = __builtin_amdgcn_alignbit(m, hit ? 0u : 0x80000000u, 31);
+    } else {
+      m = __builtin_amdgcn_alignbit(m, __float_as_uint(x), 31);
+    }
+  }
+  return ~m;
+}
+
+// Spill the stage's values of lanes with hits to scratch, then append every
+// hit (dd, position) to the lane's segment, one hit per lane per pass.
+CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, SlabState& st,
+                         int32_t jl0, float* scr) {
+  if (hits != 0u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      reinterpret_cast<float4*>(scr)[q] =
+          make_float4(x0[4 * q], x0[4 * q + 1], x0[4 * q + 2], x0[4 * q + 3]);
+      reinterpret_cast<float4*>(scr)[4 + q] =
+          make_float4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3]);
+    }
+  }
+  while (__ballot(hits != 0u) != 0) {
+    if (hits != 0u) {
+      const int i = __builtin_ctz(hits);
+      const float dd = scr[i];
+      const int32_t pos = (jl0 + 2 * (i & 28)) | (i & 3);  // jl0 % 4 == 0
+      st.segp[st.gcnt] = ((uint64_t)__float_as_uint(dd) << 32) | (uint32_t)pos;
+      ++st.gcnt;
+      hits &= hits - 1u;
+    }
+  }
+}
+
+// grid: (nchunks, ceil(M / kFiltRows), B); wave w owns rows w*64 .. +63 of
+// the workgroup as two 32-row slabs.
+template <int D>
+__global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
+  __shared__ u32x4_t kst[2][kStageKeys * D / 8];
+  __shared__ __attribute__((aligned(16))) float scratch[kFT / kWave][kWave * kScrStride];
+  const int ch = blockIdx.x, rb = blockIdx.y, b = blockIdx.z;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int64_t key_lo = (int64_t)ch * kChunk;
+  const int m_first = rb * kFiltRows;
+  int m_last = m_first + kFiltRows - 1;
+  m_last = m_last < a.M - 1 ? m_last : a.M - 1;
+  const int64_t vis_hi = row_visible(a, b, m_last);  // visibility grows with m
+  const int64_t key_hi = key_lo + kChunk < vis_hi ? key_lo + kChunk : vis_hi;
+  const int nslab = (a.M - (m_first + w * 64) + 31) / 32;  // slabs with rows (<= 0: none)
+  float* scr = &scratch[w][lane * kScrStride];
+
+  // constant operand of the threshold k-step: 1.0 in dim 0
+  bf16x8_t kone = __builtin_bit_cast(bf16x8_t, u32x4_t{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
+  bf16x8_t qb[2][D / 16];
+  SlabState st[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int m0 = m_first + w * 64 + blk * 32;
+    const int m = m0 + lane % 32;
+    const bool ok = m < a.M;
+    load_q_slab<D>(a, b, m0, qb[blk]);
+    const float T = ok ? a.thr[(size_t)b * a.M + m] : INFINITY;
+    const bool all = T == -INFINITY;
+    st[blk].tq = __builtin_bit_cast(
+        bf16x8_t, u32x4_t{lane < 32 ? (uint32_t)(all ? 0u : neg_bf16_floor(T)) : 0u, 0u, 0u, 0u});
+    st[blk].lo = all ? -INFINITY : 0.f;
+    st[blk].lim = ok ? (int32_t)row_visible(a, b, m) : 0;
+    st[blk].lim_min = (m0 + 31 < a.M) ? (int32_t)row_visible(a, b, m0) : 0;
+    st[blk].sign_ok = __ballot(all) == 0;
+    const size_t sg = (((size_t)b * a.M + (ok ? m : 0)) * a.nchunks + ch) * 2 + lane / 32;
+    st[blk].segp = a.seg + sg * kHalf;
+    st[blk].gcnt = 0;
+  }
+  // Query operands and thresholds are in registers before the loop; with
+  // them complete, the only loads in flight inside it are the key prefetch.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+  if (key_lo < key_hi) {
+    const int nstage = (int)((key_hi - key_lo + kStageKeys - 1) / kStageKeys);
+    StageRegs<D> pre;
+    pre.load(a, b, key_lo, key_hi);
+    pre.store(kst[0]);
+    if (nstage > 1) pre.load(a, b, key_lo + kStageKeys, key_hi);
+    lds_barrier();
+    for (int sidx = 0; sidx < nstage; ++sidx) {
+      const u32x4_t* cur = kst[sidx & 1];
+      const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // stage start
+      const int32_t jl0 = js + 4 * (lane / 32);
+      bf16x8_t kb0[D / 16], kb1[D / 16];
+      load_k_tile<D>(cur, 0, kb0);
+      load_k_tile<D>(cur, 1, kb1);
+      // rows: keys, columns: queries; the last k-step subtracts T'
+      f32x16_t x[2][2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        if (blk < nslab) {
+          x[blk][0] = tile_mma<D>(kb0, qb[blk], f32x16_t{});
+          x[blk][1] = tile_mma<D>(kb1, qb[blk], f32x16_t{});
+          x[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][0], 0, 0, 0);
+          x[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][1], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        if (blk >= nslab) break;
+        SlabState& S = st[blk];
+        // wave-uniform: a scalar branch keeps the compare path out of the
+        // fast one
+        const bool fast = __builtin_amdgcn_readfirstlane(
+                              (int)(S.sign_ok && js + kStageKeys <= S.lim_min)) != 0;
+        uint32_t hits;
+        if (fast) hits = stage_hits<false>(x[blk][0], x[blk][1], S, jl0);
+        else hits = stage_hits<true>(x[blk][0], x[blk][1], S, jl0);
+        stage_emit(x[blk][0], x[blk][1], hits, S, jl0, scr);
+      }
+      if (sidx + 1 < nstage) {
+        // the next stage's keys were loaded a stage ago; its buffer was last
+        // read before the previous barrier
+        pre.store(kst[(sidx + 1) & 1]);
+        lds_barrier();
+        if (sidx + 2 < nstage) pre.load(a, b, key_lo + (int64_t)(sidx + 2) * kStageKeys, key_hi);
+      }
+    }
+  }
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int m = m_first + w * 64 + blk * 32 + lane % 32;
+    if (m < a.M) a.segcnt[(((size_t)b * a.M + m) * a.nchunks + ch) * 2 + lane / 32] = st[blk].gcnt;
+  }
+}
+
+// ------------------------------------------------------------------ select
+// q . K_idx[j] for the exact rescan; every key of the row uses this order
+template <int D>
+CLSA_DEV float row_score(const BlockArgs& a, int b, const float* qf, int64_t j) {
+  const uint16_t* kr = a.K + ((size_t)b * a.n_cap + j) * D;
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < D / 8; ++c) {
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(kr + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s = fmaf(qf[c * 8 + 2 * e], bf16_lo(v[e]), s);
+      s = fmaf(qf[c * 8 + 2 * e + 1], bf16_hi(v[e]), s);
+    }
+  }
+  return s;
+}
+
+// Exact top-k of one row from recomputed scores: a radix select of the k-th
+// key, then the positions in order (keys above it and the first `left`
+// equal to it).
+template <int D>
+CLSA_DEV void exact_rescan(const BlockArgs& a, int b, int m, int64_t n_vis, int64_t k_eff,
+                           int32_t* out, uint32_t* h, uint32_t* tmp, uint32_t* bc, uint32_t* wcnt) {
+  const int tid = threadIdx.x;
+  float qf[D];
+  {
+    const uint16_t* qr = a.q + ((size_t)b * a.M + m) * D;
+#pragma unroll
+    for (int e = 0; e < D; ++e) qf[e] = __uint_as_float((uint32_t)qr[e] << 16);
+  }
+  uint32_t left;
+  const uint32_t kstar = select_key_desc(
+      [&](uint32_t i) { return score_key(row_score<D>(a, b, qf, i)); }, (uint32_t)n_vis,
+      (uint32_t)k_eff, h, tmp, bc, &left);
+  uint32_t run = 0, eq_seen = 0;
+  for (int64_t j0 = 0; j0 < n_vis; j0 += kNT) {
+    const int64_t j = j0 + tid;
+    const uint32_t key = j < n_vis ? score_key(row_score<D>(a, b, qf, j)) : 0u;
+    const bool eq = j < n_vis && key == kstar;
+    uint32_t eq_tot;
+    const uint32_t eq_rank = eq_seen + block_rank<kNT>(eq, wcnt, &eq_tot);
+    const bool take = j < n_vis && (key > kstar || (eq && eq_rank < left));
+    uint32_t tot;
+    const uint32_t slot = run + block_rank<kNT>(take, wcnt, &tot);
+    if (take) out[slot] = (int32_t)j;
+    run += tot;
+    eq_seen += eq_tot;
+  }
+}
+
+
+// Exact rank-th largest of the keys held in registers, 1 <= rank <= the
+// number of valid keys: thread t holds k[0 .. cnt) (cnt <= NPER).  One pass
+// of a 2048-bin histogram spanning the keys' actual range; the boundary bin
+// is ranked pairwise when it holds at most kSmall keys, and refined by
+// further 11-bit passes otherwise (massive ties).  *left gets how many keys
+// equal to the result are needed to reach the rank, *eq_total how many
+// there are.
+template <int NPER>
+CLSA_DEV uint32_t kth_regs(const uint32_t (&k)[NPER], int cnt, uint32_t rank, SelScratch& S,
+                           uint32_t* left, uint32_t* eq_total) {
+  const int tid = threadIdx.x, w = tid / kWave;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int u = 0; u < NPER; ++u)
+    if (u < cnt) {
+      lo = k[u] < lo ? k[u] : lo;
+      hi = k[u] > hi ? k[u] : hi;
+    }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t l2 = __shfl_xor(lo, m), h2 = __shfl_xor(hi, m);
+    lo = l2 < lo ? l2 : lo;
+    hi = h2 > hi ? h2 : hi;
+  }
+  if (lane_id() == 0) S.lo[w] = lo, S.hi[w] = hi;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kNT / kWave; ++i) {
+    lo = S.lo[i] < lo ? S.lo[i] : lo;
+    hi = S.hi[i] > hi ? S.hi[i] : hi;
+  }
+  const uint32_t range = hi - lo;
+  int shift = range < 2048u ? 0 : (32 - __clz(range)) - 11;
+  int shift_prev = 32;
+  uint32_t prefix = 0;  // (key - lo) >> shift_prev of the keys still in play
+  for (;;) {
+    for (int i = tid; i < 2048; i += kNT) S.h[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NPER; ++u)
+      if (u < cnt) {
+        const uint32_t d = k[u] - lo;
+        if (shift_prev >= 32) atomicAdd(&S.h[d >> shift], 1u);
+        else if ((d >> shift_prev) == prefix)
+          atomicAdd(&S.h[(d >> shift) - (prefix << (shift_prev - shift))], 1u);
+      }
+    __syncthreads();
+    find_bin_desc<2048>(S.h, rank, S.tmp, S.bc);
+    const uint32_t bin = S.bc[0], r = S.bc[1], c = S.h[bin];
+    const uint32_t full = (shift_prev >= 32 ? 0u : prefix << (shift_prev - shift)) + bin;
+    if (shift == 0) {
+      *left = r;
+      *eq_total = c;
+      __syncthreads();
+      return lo + full;
+    }
+    if (c <= (uint32_t)kSmall) {
+      if (tid == 0) S.bc[2] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NPER; ++u)
+        if (u < cnt && ((k[u] - lo) >> shift) == full) S.small[atomicAdd(&S.bc[2], 1u)] = k[u];
+      __syncthreads();
+      for (uint32_t e = tid; e < c; e += kNT) {
+        const uint32_t v = S.small[e];
+        uint32_t gt = 0, eq = 0;
+        for (uint32_t f = 0; f < c; ++f) {
+          gt += S.small[f] > v ? 1u : 0u;
+          eq += S.small[f] == v ? 1u : 0u;
+        }
+        if (gt < r && r <= gt + eq) {  // equal keys all write the same values
+          S.bc[3] = v;
+          S.bc[4] = r - gt;
+          S.bc[5] = eq;
+        }
+      }
+      __syncthreads();
+      const uint32_t kth = S.bc[3];
+      *left = S.bc[4];
+      *eq_total = S.bc[5];
+      __syncthreads();
+      return kth;
+    }
+    rank = r;
+    prefix = full;
+    shift_prev = shift;
+    shift = shift > 11 ? shift - 11 : 0;
+    __syncthreads();
+  }
+}
+
+// Exclusive scan of n values in[] into out[] (in == out allowed); returns
+// the total.  Every thread of the block must call it.
+CLSA_DEV uint32_t block_excl_scan_arr(const uint32_t* in, uint32_t* out, int n, uint32_t* tmp,
+                                      uint32_t* bc) {
+  uint32_t run = 0;
+  for (int i0 = 0; i0 < n; i0 += kNT) {
+    const int i = i0 + (int)threadIdx.x;
+    const uint32_t v = i < n ? in[i] : 0u;
+    const uint32_t incl = block_incl_scan<kNT>(v, tmp);
+    if (i < n) out[i] = run + incl - v;
+    if (threadIdx.x == kNT - 1) bc[0] = incl;
+    __syncthreads();
+    run += bc[0];
+    __syncthreads();
+  }
+  return run;
+}
+
+// One workgroup per row.  Each thread holds a contiguous run of at most
+// kPerT candidates in registers; the row's selection is marked in a bitmap
+// over its key positions (dynamic LDS, 1024 bits per key chunk) and written
+// out in position order from a popcount prefix over the bitmap's words.
+constexpr int kPerT = kSelCap / kNT;
+
+template <int D>
+__global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
+  extern __shared__ uint32_t bitmap[];  // a.nchunks * 32 words
+  __shared__ uint32_t segoff[2 * kMaxChunks + 1];
+  __shared__ SelScratch S;
+  __shared__ uint32_t wcnt[kNT / kWave];
+
+  const int r = blockIdx.x;
+  const int b = r / a.M, m = r % a.M;
+  const int tid = threadIdx.x;
+  const int64_t n_vis = row_visible(a, b, m);
+  const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
+  int32_t* out = a.idx + (size_t)r * a.cap;
+  if (tid == 0) a.counts[r] = (int32_t)k_eff;
+  for (int64_t i = k_eff + tid; i < a.cap; i += kNT) out[i] = -1;
+  if (k_eff >= n_vis) {
+    for (int64_t i = tid; i < n_vis; i += kNT) out[i] = (int32_t)i;
+    return;
+  }
+
+  // offsets of the row's half-segments (key chunk c: segments 2c and 2c+1)
+  const int nseg = 2 * a.nchunks;
+  const uint32_t n_c = block_excl_scan_arr(a.segcnt + (size_t)r * nseg, segoff, nseg, S.tmp, S.bc);
+  if (tid == 0) segoff[nseg] = n_c;
+  __syncthreads();
+
+  if (n_c < (uint32_t)k_eff || n_c > (uint32_t)kSelCap) {
+    exact_rescan<D>(a, b, m, n_vis, k_eff, out, S.h, S.tmp, S.bc, wcnt);
+    return;
+  }
+
+  // candidates [i0, i0 + cnt): locate each one's segment first (one binary
+  // search, then a forward walk), then issue all loads at once
+  const uint32_t per = (n_c + kNT - 1) / kNT;
+  const uint32_t i0 = (uint32_t)tid * per;
+  const int cnt = i0 < n_c ? (int)(n_c - i0 < per ? n_c - i0 : per) : 0;
+  uint32_t key[kPerT], pos[kPerT];
+  {
+    int lo = 0, hi = nseg;  // segoff[lo] <= i0 < segoff[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (segoff[mid] <= i0) lo = mid;
+      else hi = mid;
+    }
+    uint32_t off[kPerT];
+    int sg = lo;
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      if (u < cnt) {
+        const uint32_t i = i0 + u;
+        while (segoff[sg + 1] <= i) ++sg;
+        off[u] = (uint32_t)sg * kHalf + (i - segoff[sg]);
+      }
+    const uint64_t* rowseg = a.seg + (size_t)r * nseg * kHalf;
+    uint64_t e[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) e[u] = u < cnt ? rowseg[off[u]] : 0ull;
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) {
+      key[u] = score_key(__uint_as_float((uint32_t)(e[u] >> 32)));
+      pos[u] = (uint32_t)e[u];
+    }
+  }
+
+  uint32_t left, eq_total;
+  const uint32_t kstar = kth_regs<kPerT>(key, cnt, (uint32_t)k_eff, S, &left, &eq_total);
+
+  // mark the selection: keys above kstar, and of the keys equal to it the
+  // `left` lowest positions
+  const int nwords = a.nchunks * 32;
+  for (int i = tid; i < nwords; i += kNT) bitmap[i] = 0u;
+  __syncthreads();
+  const int wpt = (nwords + kNT - 1) / kNT;  // bitmap words per thread, contiguous
+  const int w0 = tid * wpt;
+  if (left == eq_total) {
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      if (u < cnt && key[u] >= kstar) atomicOr(&bitmap[pos[u] >> 5], 1u << (pos[u] & 31));
+  } else if (eq_total <= (uint32_t)kSmall) {
+    if (tid == 0) S.bc[2] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      if (u < cnt && key[u] == kstar) S.small[atomicAdd(&S.bc[2], 1u)] = pos[u];
+    __syncthreads();
+    for (uint32_t e = tid; e < eq_total; e += kNT) {
+      const uint32_t p = S.small[e];
+      uint32_t lower = 0;
+      for (uint32_t f = 0; f < eq_total; ++f) lower += S.small[f] < p ? 1u : 0u;
+      if (lower < left) atomicOr(&bitmap[p >> 5], 1u << (p & 31));
+    }
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      if (u < cnt && key[u] > kstar) atomicOr(&bitmap[pos[u] >> 5], 1u << (pos[u] & 31));
+  } else {
+    // massive ties: mark every equal key, keep the first `left` in position
+    // order, then add the keys above kstar
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      if (u < cnt && key[u] == kstar) atomicOr(&bitmap[pos[u] >> 5], 1u << (pos[u] & 31));
+    __syncthreads();
+    uint32_t mine = 0;
+    for (int i = w0; i < w0 + wpt && i < nwords; ++i) mine += __popc(bitmap[i]);
+    uint32_t rank = block_incl_scan<kNT>(mine, S.tmp) - mine;
+    for (int i = w0; i < w0 + wpt && i < nwords; ++i) {
+      uint32_t word = bitmap[i];
+      for (uint32_t rest = word; rest != 0u; rest &= rest - 1u) {
+        if (rank >= left) word &= ~(rest & (0u - rest));
+        ++rank;
+      }
+      bitmap[i] = word;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      if (u < cnt && key[u] > kstar) atomicOr(&bitmap[pos[u] >> 5], 1u << (pos[u] & 31));
+  }
+  __syncthreads();
+
+  // emit in position order
+  uint32_t mine = 0;
+  for (int i = w0; i < w0 + wpt && i < nwords; ++i) mine += __popc(bitmap[i]);
+  uint32_t slot = block_incl_scan<kNT>(mine, S.tmp) - mine;
+  for (int i = w0; i < w0 + wpt && i < nwords; ++i) {
+    uint32_t word = bitmap[i];
+    while (word != 0u) {
+      const int bit = __builtin_ctz(word);
+      out[slot++] = (int32_t)((uint32_t)i * 32u + (uint32_t)bit);
+      word &= word - 1u;
+    }
+  }
+}
+
+template <int D>
+void launch_block(const BlockArgs& a, hipStream_t s) {
+  const int R = a.B * a.M;
+  hipLaunchKernelGGL(block_sample<D>,
+                     dim3((unsigned)((a.ns_max + kStageKeys - 1) / kStageKeys),
+                          (unsigned)((a.M + kSampRows - 1) / kSampRows), (unsigned)a.B),
+                     dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(block_thresh, dim3((unsigned)R), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(block_filter<D>,
+                     dim3((unsigned)a.nchunks, (unsigned)((a.M + kFiltRows - 1) / kFiltRows),
+                          (unsigned)a.B),
+                     dim3(kFT), 0, s, a);
+  hipLaunchKernelGGL(block_select<D>, dim3((unsigned)R), dim3(kNT),
+                     (size_t)a.nchunks * 32 * sizeof(uint32_t), s, a);
+}
+
+struct BlockLayout {
+  int ns_max, nchunks;
+  size_t o_samp, o_thr, o_cnt, o_seg, total;
+};
+
+BlockLayout block_layout(int64_t R, int64_t n_cap) {
+  BlockLayout L{};
+  L.ns_max = (int)ceil_div64(n_cap, kSStride);
+  L.nchunks = (int)ceil_div64(n_cap, kChunk);
+  size_t o = 0;
+  L.o_samp = o; o = align_up(o + (size_t)R * L.ns_max * 4, 256);
+  L.o_thr = o; o = align_up(o + (size_t)R * 4, 256);
+  L.o_cnt = o; o = align_up(o + (size_t)R * L.nchunks * 2 * 4, 256);
+  L.o_seg = o; o = align_up(o + (size_t)R * L.nchunks * 2 * kHalf * 8, 256);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------- host
+bool block_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt) {
+  return dt == CLSA_BF16 && M >= 64 && k <= kMaxK && (d == 32 || d == 64 || d == 128) &&
+         ceil_div64(n_cap, kChunk) <= kMaxChunks;
+}
+
+size_t block_route_workspace(int B, int M, int64_t n_cap) {
+  return block_layout((int64_t)B * M, n_cap).total;
+}
+
+int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
+                int cap, void* ws, hipStream_t s) {
+  const BlockLayout L = block_layout((int64_t)B * M, n_cap);
+  char* base = static_cast<char*>(ws);
+  BlockArgs a{};
+  a.q = static_cast<const uint16_t*>(q_idx);
+  a.K = static_cast<const uint16_t*>(K_idx);
+  a.n_ctx = n_ctx;
+  a.idx = idx;
+  a.counts = counts;
+  a.n_cap = n_cap;
+  a.q_pos0 = q_pos0 < 0 ? -1 : q_pos0;
+  a.B = B;
+  a.M = M;
+  a.k = k;
+  a.cap = cap;
+  a.ns_max = L.ns_max;
+  a.nchunks = L.nchunks;
+  a.samp = reinterpret_cast<uint32_t*>(base + L.o_samp);
+  a.thr = reinterpret_cast<float*>(base + L.o_thr);
+  a.segcnt = reinterpret_cast<uint32_t*>(base + L.o_cnt);
+  a.seg = reinterpret_cast<uint64_t*>(base + L.o_seg);
+  if (d == 32) launch_block<32>(a, s);
+  else if (d == 64) launch_block<64>(a, s);
+  else launch_block<128>(a, s);
+  return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
+}
+
+}  // namespace clsa

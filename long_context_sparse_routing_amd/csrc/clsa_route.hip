@@ -158,25 +158,6 @@ CLSA_DEV uint32_t block_sum_prefix(const uint32_t* arr, int64_t n, uint32_t* tmp
   return s;
 }
 
-// Ordered compaction of one 256-key slice: returns this thread's slot among
-// the set predicates of the slice (ascending thread order) and the slice's
-// total in *total.
-CLSA_DEV uint32_t block_rank(bool p, uint32_t* wcnt, uint32_t* total) {
-  const int w = threadIdx.x / kWave;
-  const uint64_t mask = __ballot(p);
-  if (lane_id() == 0) wcnt[w] = (uint32_t)__popcll(mask);
-  __syncthreads();
-  uint32_t before = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kNT / kWave; ++i) {
-    before += (i < w) ? wcnt[i] : 0u;
-    tot += wcnt[i];
-  }
-  __syncthreads();
-  *total = tot;
-  return before + lanes_below(mask);
-}
-
 // ------------------------------------------------------------------- score
 template <typename T, int D, bool TOPK>
 __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
@@ -658,14 +639,22 @@ RouteArgs fill_args(const Layout& L, void* ws, const void* q_idx, const void* K_
 }
 
 }  // namespace
+
+// Block routing on the matrix cores (clsa_prefill.hip): bf16 keys, many
+// query rows per sequence.
+bool block_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt);
+size_t block_route_workspace(int B, int M, int64_t n_cap);
+int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
+                int cap, void* ws, hipStream_t s);
 }  // namespace clsa
 
 using namespace clsa;
 
 extern "C" size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, int k, int cap,
                                             clsa_dtype dt) {
-  (void)dt;
   if (!shape_ok(B, M, d, n_cap, cap) || k < 1) return 0;
+  if (block_route_applies(M, d, n_cap, k, dt)) return block_route_workspace(B, M, n_cap);
   return make_layout((int64_t)B * M, n_cap, true).total;
 }
 
@@ -676,10 +665,14 @@ extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, in
   if (dt != CLSA_F32 && dt != CLSA_BF16) return CLSA_ERR_UNSUPPORTED_DTYPE;
   if (!q_idx || !K_idx || !idx || !counts) return CLSA_ERR_INVALID;
   if (!shape_ok(B, M, d, n_cap, cap) || k < 1 || cap < k) return CLSA_ERR_INVALID;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (block_route_applies(M, d, n_cap, k, dt)) {
+    if (!ws || ws_bytes < block_route_workspace(B, M, n_cap)) return CLSA_ERR_WORKSPACE;
+    return block_route(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, ws, s);
+  }
   const int64_t R = (int64_t)B * M;
   const Layout L = make_layout(R, n_cap, true);
   if (!ws || ws_bytes < L.total) return CLSA_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
   const RouteArgs a = fill_args(L, ws, q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, k, nullptr,
                                 idx, counts, cap);
   if (zero_fill(ws, L.ctrl_end, s) != hipSuccess) return CLSA_ERR_HIP;

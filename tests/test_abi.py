@@ -65,6 +65,10 @@ def test_route_workspace_sizes(lib):
     assert big >= 8 * 131136 * 12
     assert lib.clsa_route_workspace_size(1, 1, 48, 4096, 256, 256, BF16) == 0  # bad d
     assert lib.clsa_route_threshold_workspace_size(16, 1, 128, 131072, 16384, BF16) > 0
+    # a block of query rows on bf16 keys: sampled keys and candidate segments
+    blk = lib.clsa_route_workspace_size(1, 4096, 128, 131136, 2048, 2048, BF16)
+    assert blk >= 4096 * 131136 * 8
+    assert lib.clsa_route_workspace_size(1, 4096, 128, 131136, 2048, 2048, F32) > 0
 
 
 def test_attn_workspace_sizes(lib):
