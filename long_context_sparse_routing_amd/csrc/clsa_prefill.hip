@@ -8,17 +8,17 @@
 // dense contraction, so they run on v_mfma_f32_32x32x16_bf16 and the score
 // matrix never reaches HBM.
 //
-//   block_sample   scores of every row against every kSStride-th key (MFMA),
-//                  stored as order-preserving keys.
-//   block_thresh   per row, the rho-th largest sampled score (exact radix
-//                  select), rho chosen so that, with a four-sigma margin,
-//                  at least k keys of the row score that much.  It becomes
-//                  the row's filter threshold T.
+//   block_thresh   per group of 16 rows: scores against every ss-th key
+//                  (MFMA), kept in LDS as 16-bit key prefixes; per row a
+//                  lower bound of the rho-th largest sampled score, rho
+//                  chosen so that, with a four-sigma margin, at least k keys
+//                  of the row score that much.  It becomes the row's filter
+//                  threshold T.
 //   block_filter   the full score matrix in 32x32 MFMA tiles, keys as the A
 //                  operand and queries as B, so each lane owns one query
-//                  column; keys scoring >= T are appended as (score,
-//                  position) to a segment of the lane's own, through a small
-//                  LDS ring: no atomics, no cross-lane work per hit.
+//                  column; a workgroup keeps one key chunk in LDS and streams
+//                  query rows through it.  Keys scoring >= T are appended as
+//                  (score - T', position) to a segment of the lane's own.
 //   block_select   per row: the exact top-k among the candidates (lower
 //                  positions win ties), written in ascending order.  A row
 //                  whose threshold kept fewer than k keys, or more than the
@@ -30,18 +30,18 @@
 namespace clsa {
 namespace {
 
-constexpr int kNT = 256;           // threads of the sample/thresh/select kernels
-constexpr int kFT = 256;           // threads of the filter kernel (4 waves)
+constexpr int kNT = 256;           // threads of the thresh/select kernels
+constexpr int kFT = 512;           // threads of the filter kernel (8 waves)
 constexpr int kSStride = 32;       // sampling stride of the threshold estimate
-constexpr int kSampRows = 256;     // rows per sample workgroup (4 waves x 64)
-constexpr int kFiltRows = 256;     // rows per filter workgroup (4 waves x 64)
-constexpr int kChunk = 1024;       // keys per filter workgroup
-constexpr int kHalf = kChunk / 2;  // keys one half-wave scores per chunk
-constexpr int kStageKeys = 64;     // keys staged in LDS per step
+constexpr int kStageKeys = 64;     // keys per filter step (two 32-key tiles)
 constexpr int kSelCap = 6144;      // candidates a select workgroup holds
 constexpr int kMaxK = 2048;
-constexpr int kMaxChunks = 512;    // key chunks per row
-constexpr int kThrLds = 8192;      // sampled keys the thresh kernel holds
+constexpr int kMaxSegs = 2048;     // half-segments per row
+constexpr int64_t kMaxKeys = 524288;
+
+// Keys per filter chunk: the chunk stays in LDS for the workgroup's life,
+// 64 KB of bf16 keys.
+constexpr int chunk_keys(int d) { return 32768 / d; }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -54,12 +54,14 @@ struct BlockArgs {
   int32_t* counts;         // [B][M]
   int64_t n_cap, q_pos0;
   int B, M, k, cap;
-  int ns_max;              // sampled keys per row (max)
+  int ns_max;              // sampled keys per row (max, <= kThrNs)
+  int64_t ss;              // sampling stride (keys)
+  int kc;                  // keys per chunk (chunk_keys(d))
   int nchunks;             // key chunks per row
-  uint32_t* samp;          // [R][ns_max] sampled score keys
+  int rows_pg;             // rows per filter workgroup (multiple of 64)
   float* thr;              // [R] filter threshold; -inf: every key, +inf: none
   uint32_t* segcnt;        // [R][nchunks][2] candidates per half-segment
-  uint64_t* seg;           // [R][nchunks][2][kHalf]: position | score << 32
+  uint64_t* seg;           // [R][nchunks][2][kc/2]: position | (score - T') << 32
 };
 
 CLSA_DEV int64_t row_visible(const BlockArgs& a, int b, int m) {
@@ -98,20 +100,6 @@ CLSA_DEV int lds_piece(int n, int c) {
   return n * P + (c ^ (n & (P - 1)));
 }
 
-// keys key0 + n*stride (n < kStageKeys) into LDS, zeros at positions >= n_lim
-template <int D, int NT>
-CLSA_DEV void stage_keys(const BlockArgs& a, int b, int64_t key0, int64_t stride, int64_t n_lim,
-                         u32x4_t* lds) {
-  constexpr int P = D / 8;
-  for (int i = threadIdx.x; i < kStageKeys * P; i += NT) {
-    const int n = i / P, c = i % P;
-    const int64_t j = key0 + (int64_t)n * stride;
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (j < n_lim) v = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + c * 8);
-    lds[lds_piece<D>(n, c)] = v;
-  }
-}
-
 template <int D>
 CLSA_DEV void load_k_tile(const u32x4_t* lds, int t, bf16x8_t (&kb)[D / 16]) {
   const int lane = lane_id();
@@ -132,41 +120,6 @@ CLSA_DEV f32x16_t tile_mma(const bf16x8_t (&x)[D / 16], const bf16x8_t (&y)[D / 
 
 // row of accumulator value v held by lane l (its column is l % 32)
 CLSA_DEV int acc_row(int v, int lane) { return 8 * (v / 4) + 4 * (lane / 32) + (v % 4); }
-
-// ------------------------------------------------------------------ sample
-// grid: (ceil(ns_max / kStageKeys), ceil(M / kSampRows), B)
-template <int D>
-__global__ __launch_bounds__(kNT) void block_sample(BlockArgs a) {
-  __shared__ u32x4_t kst[kStageKeys * D / 8];
-  const int sc = blockIdx.x, rb = blockIdx.y, b = blockIdx.z;
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int64_t s0 = (int64_t)sc * kStageKeys;
-  stage_keys<D, kNT>(a, b, s0 * kSStride, kSStride, a.n_cap, kst);
-  __syncthreads();
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int m0 = rb * kSampRows + w * 64 + blk * 32;
-    if (m0 >= a.M) break;
-    bf16x8_t qa[D / 16];
-    load_q_slab<D>(a, b, m0, qa);
-#pragma unroll
-    for (int t = 0; t < kStageKeys / 32; ++t) {
-      bf16x8_t kb[D / 16];
-      load_k_tile<D>(kst, t, kb);
-      const f32x16_t c = tile_mma<D>(qa, kb, f32x16_t{});  // rows: queries, columns: samples
-      const int64_t s = s0 + t * 32 + lane % 32;
-      const int64_t j = s * kSStride;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + acc_row(v, lane);
-        if (m < a.M && s < a.ns_max) {
-          const bool vis = j < row_visible(a, b, m);
-          a.samp[((size_t)b * a.M + m) * a.ns_max + s] = vis ? score_key(c[v]) : 0u;
-        }
-      }
-    }
-  }
-}
 
 // ----------------------------------------------------- LDS radix helpers
 // Bin holding the rank-th largest element of histogram h[0..NB) (bin NB-1
@@ -229,7 +182,7 @@ CLSA_DEV uint32_t select_key_desc(Get get, uint32_t n, uint32_t rank, uint32_t* 
 
 constexpr int kSmall = 256;  // boundary-bin elements ranked pairwise
 
-struct SelScratch {  // LDS scratch of select_kth_desc
+struct SelScratch {  // LDS scratch of the block selects
   uint32_t h[2048];
   uint32_t small[kSmall];
   uint32_t tmp[kNT / kWave];
@@ -237,143 +190,201 @@ struct SelScratch {  // LDS scratch of select_kth_desc
   uint32_t bc[8];
 };
 
-// Exact rank-th largest of the n keys get(0 .. n-1), 1 <= rank <= n; *left
-// gets how many elements equal to it are needed to reach the rank.  One
-// histogram pass over 2048 bins spanning the keys' actual range [lo, hi]
-// (so a narrow range still spreads out), then the boundary bin's elements
-// are ranked pairwise.  A boundary bin above kSmall elements (massive ties)
-// falls back to the full three-pass radix select.
-template <class Get>
-CLSA_DEV uint32_t select_kth_desc(Get get, uint32_t n, uint32_t rank, SelScratch& S,
-                                  uint32_t* left) {
-  const int tid = threadIdx.x, w = tid / kWave;
-  uint32_t lo = 0xffffffffu, hi = 0u;
-  for (uint32_t i = tid; i < n; i += kNT) {
-    const uint32_t k = get(i);
-    lo = k < lo ? k : lo;
-    hi = k > hi ? k : hi;
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t l2 = __shfl_xor(lo, m), h2 = __shfl_xor(hi, m);
-    lo = l2 < lo ? l2 : lo;
-    hi = h2 > hi ? h2 : hi;
-  }
-  if (lane_id() == 0) S.lo[w] = lo, S.hi[w] = hi;
-  for (int i = tid; i < 2048; i += kNT) S.h[i] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < kNT / kWave; ++i) {
-    lo = S.lo[i] < lo ? S.lo[i] : lo;
-    hi = S.hi[i] > hi ? S.hi[i] : hi;
-  }
-  const uint32_t range = hi - lo;
-  const int shift = range < 2048u ? 0 : (32 - __clz(range)) - 11;
-  for (uint32_t i = tid; i < n; i += kNT) atomicAdd(&S.h[(get(i) - lo) >> shift], 1u);
-  __syncthreads();
-  find_bin_desc<2048>(S.h, rank, S.tmp, S.bc);
-  const uint32_t bin = S.bc[0], r1 = S.bc[1], c1 = S.h[bin];
-  if (c1 > (uint32_t)kSmall) {
-    __syncthreads();
-    return select_key_desc(get, n, rank, S.h, S.tmp, S.bc, left);
-  }
-  if (tid == 0) S.bc[2] = 0u;
-  __syncthreads();
-  for (uint32_t i = tid; i < n; i += kNT) {
-    const uint32_t k = get(i);
-    if (((k - lo) >> shift) == bin) S.small[atomicAdd(&S.bc[2], 1u)] = k;
-  }
-  __syncthreads();
-  for (uint32_t e = tid; e < c1; e += kNT) {
-    const uint32_t v = S.small[e];
-    uint32_t gt = 0, eq = 0;
-    for (uint32_t f = 0; f < c1; ++f) {
-      gt += S.small[f] > v ? 1u : 0u;
-      eq += S.small[f] == v ? 1u : 0u;
-    }
-    if (gt < r1 && r1 <= gt + eq) {  // equal elements all write the same values
-      S.bc[3] = v;
-      S.bc[4] = r1 - gt;
-    }
-  }
-  __syncthreads();
-  const uint32_t kth = S.bc[3];
-  *left = S.bc[4];
-  __syncthreads();
-  return kth;
-}
-
 // inverse of score_key
 CLSA_DEV float key_to_float(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
 // ------------------------------------------------------------------ thresh
-// one workgroup per row
+// One workgroup per 16 query rows.  Scores against every a.ss-th key come
+// from v_mfma_f32_16x16x32_bf16 and stay in LDS as the top 16 bits of their
+// order-preserving keys.  Each wave then takes its rows one at a time: the
+// samples go to registers, a 1024-bin histogram spans their actual key range
+// and a second pass resolves the boundary bin, which gives the rho-th
+// largest 16-bit key; the threshold is the smallest float with that key
+// prefix -- never above the sample.  rho is the smallest
+// count with rho - 4 sqrt(rho) >= k * ns / n, so at least k keys of the row
+// score above the threshold with high probability; rows where it keeps
+// fewer (or too many) keys are caught by the select.
+constexpr int kThrRows = 16;  // rows per workgroup: one 16-row MFMA block
+constexpr int kThrNs = 4096;  // sampled keys per row at most
+constexpr int kThrTiles = 8;  // 16-sample tiles whose loads are in flight together
+constexpr int kThrBins = 1024;
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
 __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
-  __shared__ uint32_t ks[kThrLds];
-  __shared__ SelScratch S;
-  const int r = blockIdx.x;
-  const int b = r / a.M, m = r % a.M;
-  const int64_t n_vis = row_visible(a, b, m);
-  const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
-  if (k_eff >= n_vis) {  // every visible key is selected: no candidates needed
-    if (threadIdx.x == 0) a.thr[r] = INFINITY;
-    return;
-  }
-  const int64_t ns = (n_vis + kSStride - 1) / kSStride;
-  // smallest rho with rho - 4 sqrt(rho) >= k_eff * ns / n_vis
-  const float kappa = (float)k_eff * (float)ns / (float)n_vis;
-  const float sr = 2.0f + sqrtf(4.0f + kappa);
-  const int64_t rho = (int64_t)ceilf(sr * sr);
-  if (rho > ns) {  // too few samples to bound the k-th score: keep every key
-    if (threadIdx.x == 0) a.thr[r] = -INFINITY;
-    return;
-  }
-  const uint32_t* srow = a.samp + (size_t)r * a.ns_max;
-  const bool in_lds = ns <= kThrLds;
-  if (in_lds) {  // eight independent loads in flight per thread
-    for (int64_t i0 = 0; i0 < ns; i0 += 8 * kNT) {
-      uint32_t v[8];
+  __shared__ uint16_t sk[kThrRows][kThrNs];
+  __shared__ uint32_t wh[kNT / kWave][kThrBins];
+  const int m0 = blockIdx.x * kThrRows, b = blockIdx.y;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+
+  // A operand: row m0 + lane%16, dims 32*st + 8*(lane/16) .. +7
+  bf16x8_t qa[D / 32];
+  {
+    const int m = m0 + lane % 16;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + u * kNT + threadIdx.x;
-        v[u] = i < ns ? srow[i] : 0u;
-      }
+    for (int st = 0; st < D / 32; ++st) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (m < a.M)
+        v = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)b * a.M + m) * D + 32 * st +
+                                                8 * (lane / 16));
+      qa[st] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // accumulator value j of this lane is row 4*(lane/16) + j, sample lane%16
+  int64_t lim[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t i = i0 + u * kNT + threadIdx.x;
-        if (i < ns) ks[i] = v[u];
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + 4 * (lane / 16) + j;
+    lim[j] = m < a.M ? row_visible(a, b, m) : 0;
+  }
+  const int ntile = (a.ns_max + 15) / 16;
+  for (int t0 = w * kThrTiles; t0 < ntile; t0 += (kNT / kWave) * kThrTiles) {
+    bf16x8_t kb[kThrTiles][D / 32];
+#pragma unroll
+    for (int u = 0; u < kThrTiles; ++u) {
+      const int64_t smp = (int64_t)(t0 + u) * 16 + lane % 16;
+      const int64_t j = smp * a.ss;
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st) {
+        u32x4_t v = {0u, 0u, 0u, 0u};
+        if (t0 + u < ntile && smp < a.ns_max && j < a.n_cap)
+          v = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + 32 * st +
+                                                  8 * (lane / 16));
+        kb[u][st] = __builtin_bit_cast(bf16x8_t, v);
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kThrTiles; ++u) {
+      if (t0 + u >= ntile) break;
+      f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < D / 32; ++st)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], kb[u][st], c, 0, 0, 0);
+      const int smp = (t0 + u) * 16 + lane % 16;
+      if (smp < a.ns_max) {
+        const int64_t j = (int64_t)smp * a.ss;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          sk[4 * (lane / 16) + jj][smp] = j < lim[jj] ? (uint16_t)(score_key(c[jj]) >> 16) : 0;
+      }
+    }
   }
-  uint32_t left;
-  const uint32_t key = select_kth_desc([&](uint32_t i) { return in_lds ? ks[i] : srow[i]; },
-                                       (uint32_t)ns, (uint32_t)rho, S, &left);
-  if (threadIdx.x == 0) a.thr[r] = key_to_float(key);
+  __syncthreads();
+
+  uint32_t* h = wh[w];
+  for (int rl = w; rl < kThrRows; rl += kNT / kWave) {
+    const int m = m0 + rl;
+    if (m >= a.M) break;
+    const int r = b * a.M + m;
+    const int64_t n_vis = row_visible(a, b, m);
+    const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
+    if (k_eff >= n_vis) {  // every visible key is selected: no candidates needed
+      if (lane == 0) a.thr[r] = INFINITY;
+      continue;
+    }
+    const int ns = (int)((n_vis + a.ss - 1) / a.ss);  // visible samples
+    const float kappa = (float)k_eff * (float)ns / (float)n_vis;
+    const float sr = 2.0f + sqrtf(4.0f + kappa);
+    const int64_t rho = (int64_t)ceilf(sr * sr);
+    if (rho > ns) {  // too few samples to bound the k-th score: keep every key
+      if (lane == 0) a.thr[r] = -INFINITY;
+      continue;
+    }
+    // the row's samples in registers (lane l: samples l, l+64, ...)
+    const uint16_t* row = sk[rl];
+    uint32_t v[kThrNs / kWave];
+    uint32_t lo = 0xffffu, hi = 0u;
+#pragma unroll
+    for (int u = 0; u < kThrNs / kWave; ++u) {
+      const int i = lane + u * kWave;
+      v[u] = i < ns ? row[i] : 0u;
+      if (i < ns) {
+        lo = v[u] < lo ? v[u] : lo;
+        hi = v[u] > hi ? v[u] : hi;
+      }
+    }
+#pragma unroll
+    for (int mm = 32; mm >= 1; mm >>= 1) {
+      const uint32_t l2 = __shfl_xor(lo, mm), h2 = __shfl_xor(hi, mm);
+      lo = l2 < lo ? l2 : lo;
+      hi = h2 > hi ? h2 : hi;
+    }
+    // one histogram over the row's actual key range; the threshold is the
+    // lower edge of the bin holding the rho-th largest sample (<= it)
+    const uint32_t range = hi - lo;
+    const int shift = range < kThrBins ? 0 : (32 - __clz(range)) - 10;
+#pragma unroll
+    for (int i = 0; i < kThrBins / kWave; ++i) h[lane + kWave * i] = 0u;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < kThrNs / kWave; ++u)
+      if (lane + u * kWave < ns) atomicAdd(&h[(v[u] - lo) >> shift], 1u);
+    __builtin_amdgcn_wave_barrier();
+    // bins in descending order: lane l holds bins 1023-16l .. 1008-16l
+    uint32_t c[kThrBins / kWave], sum = 0;
+#pragma unroll
+    for (int i = 0; i < kThrBins / kWave; ++i) {
+      c[i] = h[kThrBins - 1 - (kThrBins / kWave) * lane - i];
+      sum += c[i];
+    }
+    const uint32_t incl = wave_incl_scan(sum);
+    const bool mine = incl - sum < (uint32_t)rho && (uint32_t)rho <= incl;
+    uint32_t bin = 0, rin = 0;  // bin of the rho-th largest, its rank inside
+    if (mine) {
+      uint32_t acc = incl - sum;
+#pragma unroll
+      for (int i = 0; i < kThrBins / kWave; ++i) {
+        if (acc + c[i] >= (uint32_t)rho) {
+          bin = kThrBins - 1 - (kThrBins / kWave) * lane - i;
+          rin = (uint32_t)rho - acc;
+          break;
+        }
+        acc += c[i];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    bin = __shfl(bin, src);
+    rin = __shfl(rin, src);
+    uint32_t kth = lo + (bin << shift);  // 16-bit key of the rho-th largest
+    if (shift > 0) {
+      // second pass: the bin's 2^shift (<= 64) keys, exactly
+      __builtin_amdgcn_wave_barrier();
+      h[lane] = 0u;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < kThrNs / kWave; ++u)
+        if (lane + u * kWave < ns && (v[u] - kth) < (1u << shift)) atomicAdd(&h[v[u] - kth], 1u);
+      __builtin_amdgcn_wave_barrier();
+      const uint32_t cc = lane < (1 << shift) ? h[(1 << shift) - 1 - lane] : 0u;  // descending
+      const uint32_t inc2 = wave_incl_scan(cc);
+      const bool mine2 = inc2 - cc < rin && rin <= inc2;
+      const int src2 = __ffsll((unsigned long long)__ballot(mine2)) - 1;
+      kth += (uint32_t)((1 << shift) - 1 - src2);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // smallest float of the 16-bit bucket: never above the sample
+    if (lane == 0) a.thr[r] = key_to_float(kth << 16);
+  }
 }
 
 // ------------------------------------------------------------------ filter
-// Each workgroup scores kFiltRows query rows against one chunk of kChunk
-// keys, staged through LDS kStageKeys at a time (the next stage's keys are
-// loaded into registers while the current one is scored).
+// Each workgroup holds one chunk of chunk_keys(d) keys in LDS for its whole
+// life and its 8 waves stream 64-row query slab pairs through registers:
+// no barrier inside the loop, and the chunk is read from HBM once per
+// workgroup.
 //
-// A fifth MFMA k-step against a constant column subtracts the row's
+// A last MFMA k-step against a constant column subtracts the row's
 // threshold inside the accumulator: dd = score - T', with T' the threshold
 // rounded down to bf16 (still a lower bound, so nothing is lost).  The sign
-// bits of a stage's 32 values per lane then pack into one hit mask with one
+// bits of a step's 32 values per lane pack into one hit mask with one
 // v_alignbit each; lanes with hits spill their 32 values to LDS scratch and
-// a loop over set bits, all lanes in parallel, appends (dd, position) to the
+// up to four hits per lane per pass are appended as (dd, position) to the
 // lane's segment in HBM.  Rows that keep every key (threshold -inf) and
 // tiles crossing a row's visibility limit take explicit compares instead.
 constexpr int kScrStride = 36;  // scratch words per lane (32 values, padded
                                 // so 16 consecutive lanes hit distinct banks)
-
-// Workgroup barrier for LDS traffic only.  __syncthreads() would also wait
-// for every outstanding global load, which defeats the key prefetch; the
-// "memory" clobber keeps the compiler from moving LDS accesses across it.
-CLSA_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // bf16 bits of -x, with x first rounded down to bf16 (toward -inf)
 CLSA_DEV uint16_t neg_bf16_floor(float x) {
@@ -383,34 +394,6 @@ CLSA_DEV uint16_t neg_bf16_floor(float x) {
   u = (t != u && (u >> 31)) ? t + 0x10000u : t;  // negative: away from zero
   return (uint16_t)((u ^ 0x80000000u) >> 16);
 }
-
-// Keys [key0, key0 + kStageKeys) as 16-byte pieces, kFT threads: piece
-// i = threadIdx.x + u*kFT is key i / (D/8), dims 8*(i % (D/8)) ..; keys at or
-// beyond key_hi read as zeros.
-template <int D>
-struct StageRegs {
-  static constexpr int kPieces = kStageKeys * D / 8;
-  static constexpr int kPer = (kPieces + kFT - 1) / kFT;
-  u32x4_t v[kPer];
-
-  CLSA_DEV void load(const BlockArgs& a, int b, int64_t key0, int64_t key_hi) {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = threadIdx.x + u * kFT;
-      const int64_t j = key0 + i / (D / 8);
-      v[u] = u32x4_t{0u, 0u, 0u, 0u};
-      if (i < kPieces && j < key_hi)
-        v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % (D / 8)) * 8);
-    }
-  }
-  CLSA_DEV void store(u32x4_t* lds) const {
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-      const int i = threadIdx.x + u * kFT;
-      if (i < kPieces) lds[lds_piece<D>(i / (D / 8), i % (D / 8))] = v[u];
-    }
-  }
-};
 
 struct SlabState {
   bf16x8_t tq;      // k-step operand: -T' in dim 0 (lanes < 32)
@@ -422,7 +405,7 @@ struct SlabState {
   uint32_t gcnt;    // entries written there
 };
 
-// One stage (two 32-key tiles) of one slab: the 32 values of this lane's
+// One step (two 32-key tiles) of one slab: the 32 values of this lane's
 // query, value i being key jl0 + 2*(i & 28) + (i & 3).  Returns the hit
 // mask, bit i for value i.
 template <bool CHECK>
@@ -446,8 +429,9 @@ CLSA_DEV uint32_t stage_hits(const f32x16_t& x0, const f32x16_t& x1, const SlabS
   return ~m;
 }
 
-// Spill the stage's values of lanes with hits to scratch, then append every
-// hit (dd, position) to the lane's segment, one hit per lane per pass.
+// Spill the step's values of lanes with hits to scratch, then append the
+// hits (dd, position) to the lane's segment, up to four per lane per pass
+// so that each pass waits on LDS once.
 CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, SlabState& st,
                          int32_t jl0, float* scr) {
   if (hits != 0u) {
@@ -460,41 +444,36 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
     }
   }
   while (__ballot(hits != 0u) != 0) {
-    if (hits != 0u) {
-      const int i = __builtin_ctz(hits);
-      const float dd = scr[i];
-      const int32_t pos = (jl0 + 2 * (i & 28)) | (i & 3);  // jl0 % 4 == 0
-      st.segp[st.gcnt] = ((uint64_t)__float_as_uint(dd) << 32) | (uint32_t)pos;
-      ++st.gcnt;
-      hits &= hits - 1u;
+    int idx[4];
+    float dv[4];
+    uint32_t h = hits;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      idx[q] = h != 0u ? __builtin_ctz(h) : 0;
+      h &= h - 1u;
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q]];
+    const uint32_t n = __popc(hits) - __popc(h);  // hits taken this pass (<= 4)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if ((uint32_t)q < n) {
+        const int32_t pos = (jl0 + 2 * (idx[q] & 28)) | (idx[q] & 3);  // jl0 % 4 == 0
+        st.segp[st.gcnt + q] = ((uint64_t)__float_as_uint(dv[q]) << 32) | (uint32_t)pos;
+      }
+    st.gcnt += n;
+    hits = h;
   }
 }
 
-// grid: (nchunks, ceil(M / kFiltRows), B); wave w owns rows w*64 .. +63 of
-// the workgroup as two 32-row slabs.
+// Query operands and per-row state of the slab pair at rows p0 .. p0+63
 template <int D>
-__global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
-  __shared__ u32x4_t kst[2][kStageKeys * D / 8];
-  __shared__ __attribute__((aligned(16))) float scratch[kFT / kWave][kWave * kScrStride];
-  const int ch = blockIdx.x, rb = blockIdx.y, b = blockIdx.z;
-  const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int64_t key_lo = (int64_t)ch * kChunk;
-  const int m_first = rb * kFiltRows;
-  int m_last = m_first + kFiltRows - 1;
-  m_last = m_last < a.M - 1 ? m_last : a.M - 1;
-  const int64_t vis_hi = row_visible(a, b, m_last);  // visibility grows with m
-  const int64_t key_hi = key_lo + kChunk < vis_hi ? key_lo + kChunk : vis_hi;
-  const int nslab = (a.M - (m_first + w * 64) + 31) / 32;  // slabs with rows (<= 0: none)
-  float* scr = &scratch[w][lane * kScrStride];
-
-  // constant operand of the threshold k-step: 1.0 in dim 0
-  bf16x8_t kone = __builtin_bit_cast(bf16x8_t, u32x4_t{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
-  bf16x8_t qb[2][D / 16];
-  SlabState st[2];
+CLSA_DEV void load_pair(const BlockArgs& a, int b, int p0, int ch, bf16x8_t (&qb)[2][D / 16],
+                        SlabState (&st)[2]) {
+  const int lane = lane_id();
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
-    const int m0 = m_first + w * 64 + blk * 32;
+    const int m0 = p0 + blk * 32;
     const int m = m0 + lane % 32;
     const bool ok = m < a.M;
     load_q_slab<D>(a, b, m0, qb[blk]);
@@ -507,27 +486,68 @@ __global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
     st[blk].lim_min = (m0 + 31 < a.M) ? (int32_t)row_visible(a, b, m0) : 0;
     st[blk].sign_ok = __ballot(all) == 0;
     const size_t sg = (((size_t)b * a.M + (ok ? m : 0)) * a.nchunks + ch) * 2 + lane / 32;
-    st[blk].segp = a.seg + sg * kHalf;
+    st[blk].segp = a.seg + sg * (size_t)(a.kc / 2);
     st[blk].gcnt = 0;
   }
-  // Query operands and thresholds are in registers before the loop; with
-  // them complete, the only loads in flight inside it are the key prefetch.
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+}
 
+// grid: (nchunks, ceil(M / rows_pg), B)
+template <int D>
+__global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
+  constexpr int KC = chunk_keys(D);
+  constexpr int P = D / 8;  // 16-byte pieces per key
+  __shared__ u32x4_t kc[KC * P];
+  __shared__ __attribute__((aligned(16))) float scratch[kFT / kWave][kWave * kScrStride];
+  const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int64_t key_lo = (int64_t)ch * KC;
+  const int r_lo = g * a.rows_pg;
+  const int r_hi = r_lo + a.rows_pg < a.M ? r_lo + a.rows_pg : a.M;
+  const int64_t vis_hi = row_visible(a, b, r_hi - 1);  // visibility grows with m
+  const int64_t key_hi = key_lo + KC < vis_hi ? key_lo + KC : vis_hi;
+  float* scr = &scratch[w][lane * kScrStride];
+
+  // the chunk's keys, zeros at or beyond key_hi; loads issued in groups
   if (key_lo < key_hi) {
-    const int nstage = (int)((key_hi - key_lo + kStageKeys - 1) / kStageKeys);
-    StageRegs<D> pre;
-    pre.load(a, b, key_lo, key_hi);
-    pre.store(kst[0]);
-    if (nstage > 1) pre.load(a, b, key_lo + kStageKeys, key_hi);
-    lds_barrier();
+    constexpr int kPer = KC * P / kFT;
+#pragma unroll
+    for (int u0 = 0; u0 < kPer; u0 += 8) {
+      u32x4_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = threadIdx.x + (u0 + u) * kFT;
+        const int64_t j = key_lo + i / P;
+        v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (u0 + u < kPer && j < key_hi)
+          v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % P) * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = threadIdx.x + (u0 + u) * kFT;
+        if (u0 + u < kPer) kc[lds_piece<D>(i / P, i % P)] = v[u];
+      }
+    }
+  }
+  __syncthreads();
+
+  // constant operand of the threshold k-step: 1.0 in dim 0
+  const bf16x8_t kone =
+      __builtin_bit_cast(bf16x8_t, u32x4_t{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
+  for (int p0 = r_lo + w * 64; p0 < r_hi; p0 += kFT) {
+    bf16x8_t qb[2][D / 16];
+    SlabState st[2];
+    load_pair<D>(a, b, p0, ch, qb, st);
+    const int nslab = (r_hi - p0 + 31) / 32 < 2 ? 1 : 2;
+    const int p_last = p0 + 63 < r_hi - 1 ? p0 + 63 : r_hi - 1;
+    const int64_t vis_p = row_visible(a, b, p_last);
+    const int64_t hi_p = key_hi < vis_p ? key_hi : vis_p;
+    const int nstage = hi_p > key_lo ? (int)((hi_p - key_lo + kStageKeys - 1) / kStageKeys) : 0;
     for (int sidx = 0; sidx < nstage; ++sidx) {
-      const u32x4_t* cur = kst[sidx & 1];
-      const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // stage start
+      const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // step start
       const int32_t jl0 = js + 4 * (lane / 32);
       bf16x8_t kb0[D / 16], kb1[D / 16];
-      load_k_tile<D>(cur, 0, kb0);
-      load_k_tile<D>(cur, 1, kb1);
+      load_k_tile<D>(kc, 2 * sidx, kb0);
+      load_k_tile<D>(kc, 2 * sidx + 1, kb1);
       // rows: keys, columns: queries; the last k-step subtracts T'
       f32x16_t x[2][2];
 #pragma unroll
@@ -552,19 +572,12 @@ __global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
         else hits = stage_hits<true>(x[blk][0], x[blk][1], S, jl0);
         stage_emit(x[blk][0], x[blk][1], hits, S, jl0, scr);
       }
-      if (sidx + 1 < nstage) {
-        // the next stage's keys were loaded a stage ago; its buffer was last
-        // read before the previous barrier
-        pre.store(kst[(sidx + 1) & 1]);
-        lds_barrier();
-        if (sidx + 2 < nstage) pre.load(a, b, key_lo + (int64_t)(sidx + 2) * kStageKeys, key_hi);
-      }
     }
-  }
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int m = m_first + w * 64 + blk * 32 + lane % 32;
-    if (m < a.M) a.segcnt[(((size_t)b * a.M + m) * a.nchunks + ch) * 2 + lane / 32] = st[blk].gcnt;
+    for (int blk = 0; blk < 2; ++blk) {
+      const int m = p0 + blk * 32 + lane % 32;
+      if (m < a.M) a.segcnt[(((size_t)b * a.M + m) * a.nchunks + ch) * 2 + lane / 32] = st[blk].gcnt;
+    }
   }
 }
 
@@ -737,8 +750,8 @@ constexpr int kPerT = kSelCap / kNT;
 
 template <int D>
 __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
-  extern __shared__ uint32_t bitmap[];  // a.nchunks * 32 words
-  __shared__ uint32_t segoff[2 * kMaxChunks + 1];
+  extern __shared__ uint32_t bitmap[];  // ceil(n_cap / 32) words
+  __shared__ uint32_t segoff[kMaxSegs + 1];
   __shared__ SelScratch S;
   __shared__ uint32_t wcnt[kNT / kWave];
 
@@ -780,15 +793,16 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
       else hi = mid;
     }
     uint32_t off[kPerT];
+    const uint32_t half = (uint32_t)a.kc / 2;
     int sg = lo;
 #pragma unroll
     for (int u = 0; u < kPerT; ++u)
       if (u < cnt) {
         const uint32_t i = i0 + u;
         while (segoff[sg + 1] <= i) ++sg;
-        off[u] = (uint32_t)sg * kHalf + (i - segoff[sg]);
+        off[u] = (uint32_t)sg * half + (i - segoff[sg]);
       }
-    const uint64_t* rowseg = a.seg + (size_t)r * nseg * kHalf;
+    const uint64_t* rowseg = a.seg + (size_t)r * nseg * half;
     uint64_t e[kPerT];
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) e[u] = u < cnt ? rowseg[off[u]] : 0ull;
@@ -804,7 +818,7 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
 
   // mark the selection: keys above kstar, and of the keys equal to it the
   // `left` lowest positions
-  const int nwords = a.nchunks * 32;
+  const int nwords = (int)((a.n_cap + 31) / 32);
   for (int i = tid; i < nwords; i += kNT) bitmap[i] = 0u;
   __syncthreads();
   const int wpt = (nwords + kNT - 1) / kNT;  // bitmap words per thread, contiguous
@@ -871,33 +885,32 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
 template <int D>
 void launch_block(const BlockArgs& a, hipStream_t s) {
   const int R = a.B * a.M;
-  hipLaunchKernelGGL(block_sample<D>,
-                     dim3((unsigned)((a.ns_max + kStageKeys - 1) / kStageKeys),
-                          (unsigned)((a.M + kSampRows - 1) / kSampRows), (unsigned)a.B),
+  hipLaunchKernelGGL(block_thresh<D>, dim3((unsigned)((a.M + kThrRows - 1) / kThrRows), (unsigned)a.B),
                      dim3(kNT), 0, s, a);
-  hipLaunchKernelGGL(block_thresh, dim3((unsigned)R), dim3(kNT), 0, s, a);
   hipLaunchKernelGGL(block_filter<D>,
-                     dim3((unsigned)a.nchunks, (unsigned)((a.M + kFiltRows - 1) / kFiltRows),
+                     dim3((unsigned)a.nchunks, (unsigned)((a.M + a.rows_pg - 1) / a.rows_pg),
                           (unsigned)a.B),
                      dim3(kFT), 0, s, a);
   hipLaunchKernelGGL(block_select<D>, dim3((unsigned)R), dim3(kNT),
-                     (size_t)a.nchunks * 32 * sizeof(uint32_t), s, a);
+                     (size_t)((a.n_cap + 31) / 32) * sizeof(uint32_t), s, a);
 }
 
 struct BlockLayout {
-  int ns_max, nchunks;
-  size_t o_samp, o_thr, o_cnt, o_seg, total;
+  int ns_max, kc, nchunks;
+  int64_t ss;
+  size_t o_thr, o_cnt, o_seg, total;
 };
 
-BlockLayout block_layout(int64_t R, int64_t n_cap) {
+BlockLayout block_layout(int64_t R, int d, int64_t n_cap) {
   BlockLayout L{};
-  L.ns_max = (int)ceil_div64(n_cap, kSStride);
-  L.nchunks = (int)ceil_div64(n_cap, kChunk);
+  L.ss = kSStride * ceil_div64(n_cap, (int64_t)kSStride * kThrNs);
+  L.ns_max = (int)ceil_div64(n_cap, L.ss);
+  L.kc = chunk_keys(d);
+  L.nchunks = (int)ceil_div64(n_cap, L.kc);
   size_t o = 0;
-  L.o_samp = o; o = align_up(o + (size_t)R * L.ns_max * 4, 256);
   L.o_thr = o; o = align_up(o + (size_t)R * 4, 256);
   L.o_cnt = o; o = align_up(o + (size_t)R * L.nchunks * 2 * 4, 256);
-  L.o_seg = o; o = align_up(o + (size_t)R * L.nchunks * 2 * kHalf * 8, 256);
+  L.o_seg = o; o = align_up(o + (size_t)R * L.nchunks * L.kc * 8, 256);
   L.total = o;
   return L;
 }
@@ -906,18 +919,19 @@ BlockLayout block_layout(int64_t R, int64_t n_cap) {
 
 // ------------------------------------------------------------------- host
 bool block_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt) {
-  return dt == CLSA_BF16 && M >= 64 && k <= kMaxK && (d == 32 || d == 64 || d == 128) &&
-         ceil_div64(n_cap, kChunk) <= kMaxChunks;
+  if (dt != CLSA_BF16 || M < 64 || k > kMaxK) return false;
+  if (d != 32 && d != 64 && d != 128) return false;
+  return n_cap <= kMaxKeys && 2 * ceil_div64(n_cap, chunk_keys(d)) <= kMaxSegs;
 }
 
-size_t block_route_workspace(int B, int M, int64_t n_cap) {
-  return block_layout((int64_t)B * M, n_cap).total;
+size_t block_route_workspace(int B, int M, int d, int64_t n_cap) {
+  return block_layout((int64_t)B * M, d, n_cap).total;
 }
 
 int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
                 const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
                 int cap, void* ws, hipStream_t s) {
-  const BlockLayout L = block_layout((int64_t)B * M, n_cap);
+  const BlockLayout L = block_layout((int64_t)B * M, d, n_cap);
   char* base = static_cast<char*>(ws);
   BlockArgs a{};
   a.q = static_cast<const uint16_t*>(q_idx);
@@ -932,8 +946,14 @@ int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64
   a.k = k;
   a.cap = cap;
   a.ns_max = L.ns_max;
+  a.ss = L.ss;
+  a.kc = L.kc;
   a.nchunks = L.nchunks;
-  a.samp = reinterpret_cast<uint32_t*>(base + L.o_samp);
+  // rows per filter workgroup: enough workgroups to cover the chip once,
+  // in multiples of a slab pair
+  const int64_t want_groups = ceil_div64(256, (int64_t)L.nchunks * B);
+  int64_t rows_pg = ceil_div64(M, want_groups < 1 ? 1 : want_groups);
+  a.rows_pg = (int)((rows_pg + 63) / 64 * 64);
   a.thr = reinterpret_cast<float*>(base + L.o_thr);
   a.segcnt = reinterpret_cast<uint32_t*>(base + L.o_cnt);
   a.seg = reinterpret_cast<uint64_t*>(base + L.o_seg);

@@ -643,7 +643,7 @@ RouteArgs fill_args(const Layout& L, void* ws, const void* q_idx, const void* K_
 // Block routing on the matrix cores (clsa_prefill.hip): bf16 keys, many
 // query rows per sequence.
 bool block_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt);
-size_t block_route_workspace(int B, int M, int64_t n_cap);
+size_t block_route_workspace(int B, int M, int d, int64_t n_cap);
 int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
                 const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
                 int cap, void* ws, hipStream_t s);
@@ -654,7 +654,7 @@ using namespace clsa;
 extern "C" size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, int k, int cap,
                                             clsa_dtype dt) {
   if (!shape_ok(B, M, d, n_cap, cap) || k < 1) return 0;
-  if (block_route_applies(M, d, n_cap, k, dt)) return block_route_workspace(B, M, n_cap);
+  if (block_route_applies(M, d, n_cap, k, dt)) return block_route_workspace(B, M, d, n_cap);
   return make_layout((int64_t)B * M, n_cap, true).total;
 }
 
@@ -667,7 +667,7 @@ extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, in
   if (!shape_ok(B, M, d, n_cap, cap) || k < 1 || cap < k) return CLSA_ERR_INVALID;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (block_route_applies(M, d, n_cap, k, dt)) {
-    if (!ws || ws_bytes < block_route_workspace(B, M, n_cap)) return CLSA_ERR_WORKSPACE;
+    if (!ws || ws_bytes < block_route_workspace(B, M, d, n_cap)) return CLSA_ERR_WORKSPACE;
     return block_route(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, ws, s);
   }
   const int64_t R = (int64_t)B * M;
