@@ -11,7 +11,9 @@ HBM when timing starts.
 
 Prints one JSON line: decode tokens/s (8 tokens per step), the step's
 fraction of HBM peak, the attention kernel against the HBM roofline, and the
-CPU oracle timed on a bounded sample of the same workload.
+CPU oracle timed on a bounded sample of the same workload.  A second leg
+times routing of one 4096-token prefill chunk at 128K context (the score
+matrix on the matrix cores) against the bf16 MFMA roofline.
 """
 from __future__ import annotations
 
@@ -23,6 +25,7 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2516.0  # MI355X dense bf16: 256 CUs x 2.4 GHz x 4096 flop/clk
 ROOT = os.path.dirname(os.path.abspath(__file__))
 ATTN_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_decode_128k_b8.md")
 ATTN_SOURCES = ["long_context_sparse_routing_amd/csrc/clsa_attn.hip",
@@ -113,6 +116,40 @@ def cpu_baseline(wl, K_idx, Kc, Vc, q_idx, q, n, budget_s):
     }
 
 
+def prefill_routing(calls, dev):
+    """Route one prefill chunk (4096 rows at positions 126976.., 128K keys,
+    d_idx 64, k 2048, causal) `calls` times; the score matrix runs on MFMA."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+    wl = gen.WORKLOADS["prefill_128k_c4096"]
+    K_idx, u, _ = gen.gen_routing_keys(wl, dev)
+    q_idx = gen.gen_routing_query(wl, u, 0, dev)
+    call = clsa.prepare_route(q_idx, K_idx, wl.k, q_pos0=wl.q_pos0)
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    idx, counts = call.result
+    assert int(counts.min()) == wl.k and int(counts.max()) == wl.k
+    n_scores = wl.B * sum(min(wl.n_ctx, wl.q_pos0 + m + 1) for m in range(wl.M))
+    flops = 2.0 * wl.d * n_scores  # the causal score matrix
+    tflops = flops / (us * 1e-6) / 1e12
+    return {"workload": wl.name, "rows": wl.B * wl.M, "n_ctx": wl.n_ctx, "q_pos0": wl.q_pos0,
+            "k": wl.k, "d_idx": wl.d, "calls": calls, "us_per_call": us,
+            "query_tokens_per_s": wl.B * wl.M / (us * 1e-6),
+            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                         "algorithmic_flops_per_call": flops,
+                         "what": "whole clsa_route call (threshold, filter, select)"}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +158,8 @@ def main():
     ap.add_argument("--workload", default="decode_128k_b8")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work in the baseline sample (0 = skip)")
+    ap.add_argument("--prefill-calls", type=int, default=10,
+                    help="timed calls of the prefill-chunk routing leg (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
@@ -254,6 +293,8 @@ def main():
                            "frac": r_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "algorithmic_bytes_per_call": r_bytes},
     }
+    if args.prefill_calls > 0:
+        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev)
     if args.cpu_budget > 0:
         t = total_steps - 1
         res["cpu_baseline"] = cpu_baseline(wl, K_idx, Kc, Vc, q_idx_all[t], q_all[t],

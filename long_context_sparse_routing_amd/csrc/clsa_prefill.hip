@@ -39,9 +39,14 @@ constexpr int kMaxK = 2048;
 constexpr int kMaxSegs = 2048;     // half-segments per row
 constexpr int64_t kMaxKeys = 524288;
 
-// Keys per filter chunk: the chunk stays in LDS for the workgroup's life,
-// 64 KB of bf16 keys.
-constexpr int chunk_keys(int d) { return 32768 / d; }
+// Keys held in LDS by a filter workgroup at a time (64 KB of bf16 keys),
+// and keys per candidate segment: a workgroup walks kSubPerChunk of those
+// in turn, so a row's segment of one chunk covers 4x as many keys and its
+// cache lines fill before they are written back.
+constexpr int sub_keys(int d) { return 32768 / d; }
+constexpr int kSubPerChunk = 4;
+constexpr int chunk_keys(int d) { return kSubPerChunk * sub_keys(d); }
+constexpr int kMaxRowsPerGroup = 1024;  // filter rows per workgroup: <= 2 pairs per wave
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -491,92 +496,114 @@ CLSA_DEV void load_pair(const BlockArgs& a, int b, int p0, int ch, bf16x8_t (&qb
   }
 }
 
-// grid: (nchunks, ceil(M / rows_pg), B)
+// grid: (nchunks, ceil(M / rows_pg), B); rows_pg <= kMaxRowsPerGroup, a
+// multiple of 64.  Wave w owns slab pairs w, w + 8, ... of the group (two at
+// most) and keeps their segment counts across the sub-chunks.
 template <int D>
 __global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
-  constexpr int KC = chunk_keys(D);
+  constexpr int KS = sub_keys(D);
   constexpr int P = D / 8;  // 16-byte pieces per key
-  __shared__ u32x4_t kc[KC * P];
+  constexpr int kPairs = kMaxRowsPerGroup / 64 / (kFT / kWave);
+  __shared__ u32x4_t kc[KS * P];
   __shared__ __attribute__((aligned(16))) float scratch[kFT / kWave][kWave * kScrStride];
   const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  const int64_t key_lo = (int64_t)ch * KC;
   const int r_lo = g * a.rows_pg;
   const int r_hi = r_lo + a.rows_pg < a.M ? r_lo + a.rows_pg : a.M;
   const int64_t vis_hi = row_visible(a, b, r_hi - 1);  // visibility grows with m
-  const int64_t key_hi = key_lo + KC < vis_hi ? key_lo + KC : vis_hi;
   float* scr = &scratch[w][lane * kScrStride];
-
-  // the chunk's keys, zeros at or beyond key_hi; loads issued in groups
-  if (key_lo < key_hi) {
-    constexpr int kPer = KC * P / kFT;
-#pragma unroll
-    for (int u0 = 0; u0 < kPer; u0 += 8) {
-      u32x4_t v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = threadIdx.x + (u0 + u) * kFT;
-        const int64_t j = key_lo + i / P;
-        v[u] = u32x4_t{0u, 0u, 0u, 0u};
-        if (u0 + u < kPer && j < key_hi)
-          v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % P) * 8);
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = threadIdx.x + (u0 + u) * kFT;
-        if (u0 + u < kPer) kc[lds_piece<D>(i / P, i % P)] = v[u];
-      }
-    }
-  }
-  __syncthreads();
-
-  // constant operand of the threshold k-step: 1.0 in dim 0
-  const bf16x8_t kone =
+  const bf16x8_t kone =  // constant operand of the threshold k-step: 1.0 in dim 0
       __builtin_bit_cast(bf16x8_t, u32x4_t{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
-  for (int p0 = r_lo + w * 64; p0 < r_hi; p0 += kFT) {
-    bf16x8_t qb[2][D / 16];
-    SlabState st[2];
-    load_pair<D>(a, b, p0, ch, qb, st);
-    const int nslab = (r_hi - p0 + 31) / 32 < 2 ? 1 : 2;
-    const int p_last = p0 + 63 < r_hi - 1 ? p0 + 63 : r_hi - 1;
-    const int64_t vis_p = row_visible(a, b, p_last);
-    const int64_t hi_p = key_hi < vis_p ? key_hi : vis_p;
-    const int nstage = hi_p > key_lo ? (int)((hi_p - key_lo + kStageKeys - 1) / kStageKeys) : 0;
-    for (int sidx = 0; sidx < nstage; ++sidx) {
-      const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // step start
-      const int32_t jl0 = js + 4 * (lane / 32);
-      bf16x8_t kb0[D / 16], kb1[D / 16];
-      load_k_tile<D>(kc, 2 * sidx, kb0);
-      load_k_tile<D>(kc, 2 * sidx + 1, kb1);
-      // rows: keys, columns: queries; the last k-step subtracts T'
-      f32x16_t x[2][2];
+  uint32_t gcnt[kPairs][2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        if (blk < nslab) {
-          x[blk][0] = tile_mma<D>(kb0, qb[blk], f32x16_t{});
-          x[blk][1] = tile_mma<D>(kb1, qb[blk], f32x16_t{});
-          x[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][0], 0, 0, 0);
-          x[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][1], 0, 0, 0);
+  for (int pp = 0; pp < kPairs; ++pp) gcnt[pp][0] = gcnt[pp][1] = 0u;
+
+  for (int sc = 0; sc < kSubPerChunk; ++sc) {
+    const int64_t key_lo = (int64_t)ch * a.kc + (int64_t)sc * KS;
+    const int64_t key_hi = key_lo + KS < vis_hi ? key_lo + KS : vis_hi;
+    if (key_lo >= key_hi) break;  // uniform: nothing further is visible
+    if (sc > 0) __syncthreads();  // the previous sub-chunk is no longer read
+    // the sub-chunk's keys, zeros at or beyond key_hi; loads issued in groups
+    {
+      constexpr int kPer = KS * P / kFT;
+#pragma unroll
+      for (int u0 = 0; u0 < kPer; u0 += 8) {
+        u32x4_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = threadIdx.x + (u0 + u) * kFT;
+          const int64_t j = key_lo + i / P;
+          v[u] = u32x4_t{0u, 0u, 0u, 0u};
+          if (u0 + u < kPer && j < key_hi)
+            v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % P) * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = threadIdx.x + (u0 + u) * kFT;
+          if (u0 + u < kPer) kc[lds_piece<D>(i / P, i % P)] = v[u];
         }
       }
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        if (blk >= nslab) break;
-        SlabState& S = st[blk];
-        // wave-uniform: a scalar branch keeps the compare path out of the
-        // fast one
-        const bool fast = __builtin_amdgcn_readfirstlane(
-                              (int)(S.sign_ok && js + kStageKeys <= S.lim_min)) != 0;
-        uint32_t hits;
-        if (fast) hits = stage_hits<false>(x[blk][0], x[blk][1], S, jl0);
-        else hits = stage_hits<true>(x[blk][0], x[blk][1], S, jl0);
-        stage_emit(x[blk][0], x[blk][1], hits, S, jl0, scr);
-      }
     }
+    __syncthreads();
+
+#pragma unroll
+    for (int pp = 0; pp < kPairs; ++pp) {
+      const int p0 = r_lo + (w + pp * (kFT / kWave)) * 64;
+      if (p0 >= r_hi) break;
+      bf16x8_t qb[2][D / 16];
+      SlabState st[2];
+      load_pair<D>(a, b, p0, ch, qb, st);
+      st[0].gcnt = gcnt[pp][0];
+      st[1].gcnt = gcnt[pp][1];
+      const int nslab = (r_hi - p0 + 31) / 32 < 2 ? 1 : 2;
+      const int p_last = p0 + 63 < r_hi - 1 ? p0 + 63 : r_hi - 1;
+      const int64_t vis_p = row_visible(a, b, p_last);
+      const int64_t hi_p = key_hi < vis_p ? key_hi : vis_p;
+      const int nstage = hi_p > key_lo ? (int)((hi_p - key_lo + kStageKeys - 1) / kStageKeys) : 0;
+      for (int sidx = 0; sidx < nstage; ++sidx) {
+        const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // step start
+        const int32_t jl0 = js + 4 * (lane / 32);
+        bf16x8_t kb0[D / 16], kb1[D / 16];
+        load_k_tile<D>(kc, 2 * sidx, kb0);
+        load_k_tile<D>(kc, 2 * sidx + 1, kb1);
+        // rows: keys, columns: queries; the last k-step subtracts T'
+        f32x16_t x[2][2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          if (blk < nslab) {
+            x[blk][0] = tile_mma<D>(kb0, qb[blk], f32x16_t{});
+            x[blk][1] = tile_mma<D>(kb1, qb[blk], f32x16_t{});
+            x[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][0], 0, 0, 0);
+            x[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][1], 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          if (blk >= nslab) break;
+          SlabState& S = st[blk];
+          // wave-uniform: a scalar branch keeps the compare path out of the
+          // fast one
+          const bool fast = __builtin_amdgcn_readfirstlane(
+                                (int)(S.sign_ok && js + kStageKeys <= S.lim_min)) != 0;
+          uint32_t hits;
+          if (fast) hits = stage_hits<false>(x[blk][0], x[blk][1], S, jl0);
+          else hits = stage_hits<true>(x[blk][0], x[blk][1], S, jl0);
+          stage_emit(x[blk][0], x[blk][1], hits, S, jl0, scr);
+        }
+      }
+      gcnt[pp][0] = st[0].gcnt;
+      gcnt[pp][1] = st[1].gcnt;
+    }
+  }
+  // every (row, chunk) of the group gets its count, zero when it saw nothing
+#pragma unroll
+  for (int pp = 0; pp < kPairs; ++pp) {
+    const int p0 = r_lo + (w + pp * (kFT / kWave)) * 64;
+    if (p0 >= r_hi) break;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int m = p0 + blk * 32 + lane % 32;
-      if (m < a.M) a.segcnt[(((size_t)b * a.M + m) * a.nchunks + ch) * 2 + lane / 32] = st[blk].gcnt;
+      if (m < r_hi) a.segcnt[(((size_t)b * a.M + m) * a.nchunks + ch) * 2 + lane / 32] = gcnt[pp][blk];
     }
   }
 }
@@ -953,7 +980,8 @@ int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64
   // in multiples of a slab pair
   const int64_t want_groups = ceil_div64(256, (int64_t)L.nchunks * B);
   int64_t rows_pg = ceil_div64(M, want_groups < 1 ? 1 : want_groups);
-  a.rows_pg = (int)((rows_pg + 63) / 64 * 64);
+  rows_pg = (rows_pg + 63) / 64 * 64;
+  a.rows_pg = (int)(rows_pg < kMaxRowsPerGroup ? rows_pg : kMaxRowsPerGroup);
   a.thr = reinterpret_cast<float*>(base + L.o_thr);
   a.segcnt = reinterpret_cast<uint32_t*>(base + L.o_cnt);
   a.seg = reinterpret_cast<uint64_t*>(base + L.o_seg);
