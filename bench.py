@@ -116,7 +116,33 @@ def cpu_baseline(wl, K_idx, Kc, Vc, q_idx, q, n, budget_s):
     }
 
 
-def prefill_routing(calls, dev):
+def prefill_cpu_baseline(wl, K_idx, q_idx, budget_s):
+    """Time the CPU oracle (as written) routing rows of the prefill chunk,
+    evenly spaced over the chunk, until the budget is spent."""
+    from oracle import clsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    K_np = K_idx[0].double().cpu().numpy()  # host copies: input preparation
+    q_np = q_idx[0].double().cpu().numpy()
+    done, t_tot = 0, 0.0
+    for m in range(0, wl.M, 37):
+        nv = O.visible_count(wl.n_ctx, wl.q_pos0, m)
+        t0 = time.perf_counter()
+        O.topk_select(O.route_scores(q_np[m], K_np, nv), wl.k)
+        t_tot += time.perf_counter() - t0
+        done += 1
+        if t_tot >= budget_s:
+            break
+    return {"value": done / t_tot, "unit": "query tokens/s", "cores": blas_threads,
+            "kind": "oracle",
+            "sample": (f"{done} rows of {wl.name} (every 37th row from 0: fp64 scores over "
+                       f"~{wl.n_ctx} keys, exact top-{wl.k}); NumPy BLAS threads={blas_threads}")}
+
+
+def prefill_routing(calls, dev, cpu_budget):
     """Route one prefill chunk (4096 rows at positions 126976.., 128K keys,
     d_idx 64, k 2048, causal) `calls` times; the score matrix runs on MFMA."""
     import torch
@@ -141,13 +167,83 @@ def prefill_routing(calls, dev):
     n_scores = wl.B * sum(min(wl.n_ctx, wl.q_pos0 + m + 1) for m in range(wl.M))
     flops = 2.0 * wl.d * n_scores  # the causal score matrix
     tflops = flops / (us * 1e-6) / 1e12
-    return {"workload": wl.name, "rows": wl.B * wl.M, "n_ctx": wl.n_ctx, "q_pos0": wl.q_pos0,
-            "k": wl.k, "d_idx": wl.d, "calls": calls, "us_per_call": us,
-            "query_tokens_per_s": wl.B * wl.M / (us * 1e-6),
-            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
-                         "algorithmic_flops_per_call": flops,
-                         "what": "whole clsa_route call (threshold, filter, select)"}}
+    res = {"workload": wl.name, "rows": wl.B * wl.M, "n_ctx": wl.n_ctx, "q_pos0": wl.q_pos0,
+           "k": wl.k, "d_idx": wl.d, "calls": calls, "us_per_call": us,
+           "query_tokens_per_s": wl.B * wl.M / (us * 1e-6),
+           "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
+                        "algorithmic_flops_per_call": flops,
+                        "what": "whole clsa_route call (threshold, filter, select)"}}
+    if cpu_budget > 0:
+        res["cpu_baseline"] = prefill_cpu_baseline(wl, K_idx, q_idx, cpu_budget)
+    return res
+
+
+def baselines(wl, Kc, Vc, q, n, dev, steps, shared_ms):
+    """The two designs the shared-routing path is compared with (CLSA
+    explainer, sections on compute cost and inference speed), on the same
+    caches and attention queries as the decode leg:
+      dense     -- every one of the n visible keys attended in all layers
+                   (the sparse attention call with the full position list);
+      per-layer -- each layer routes with its own index keys and query (one
+                   routing call over L*B key sets), then attends over its own
+                   list (one attention launch, layers folded into the batch).
+    Neither includes the one-row cache append of the decode step (4.5 us)."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    B, L = wl.B, wl.L
+    idx_d = torch.full((B, 1, wl.n_cap), -1, dtype=torch.int32, device=dev)
+    idx_d[:, 0, :n] = torch.arange(n, dtype=torch.int32, device=dev)
+    counts_d = torch.full((B, 1), n, dtype=torch.int32, device=dev)
+    dense = clsa.prepare_sparse_attn(q, Kc, Vc, idx_d, counts_d)
+    dense_ms = timed(dense)
+    dense_bytes = L * B * n * wl.Hkv * wl.D * 2 * 2
+    del dense, idx_d
+
+    wl_pl = wl.with_(name=wl.name + "_per_layer_keys", B=L * B, base_seed=wl.base_seed + 100)
+    K_pl, u_pl, _ = gen.gen_routing_keys(wl_pl, dev)
+    q_pl = gen.gen_routing_query(wl_pl, u_pl, 0, dev)
+    n_pl = torch.full((L * B,), n, dtype=torch.int32, device=dev)
+    route_pl = clsa.prepare_route(q_pl, K_pl, wl.k, n_ctx=n_pl)
+    idx_pl, counts_pl = route_pl.result
+    # layers folded into the batch: row l*B + b attends over layer l's cache
+    # of sequence b with its own list, all in one launch
+    fold = lambda t: t.reshape((1, L * B) + tuple(t.shape[2:]))
+    attn_pl = clsa.prepare_sparse_attn(fold(q), fold(Kc), fold(Vc), idx_pl, counts_pl)
+
+    def per_layer():
+        route_pl()
+        attn_pl()
+    route_pl_ms = timed(route_pl)
+    per_layer_ms = timed(per_layer)
+    assert int(counts_pl.min()) == wl.k and int(counts_pl.max()) == wl.k
+    del K_pl, attn_pl, route_pl
+    return {
+        "dense_attention": {"ms_per_step": dense_ms, "tokens_per_s": B / (dense_ms * 1e-3),
+                            "bytes_per_step": dense_bytes,
+                            "hbm_frac": dense_bytes / (dense_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)},
+        "per_layer_routing": {"ms_per_step": per_layer_ms, "tokens_per_s": B / (per_layer_ms * 1e-3),
+                              "route_call_ms": route_pl_ms,
+                              "attn_call_ms": per_layer_ms - route_pl_ms},
+        "shared_step_ms": shared_ms,
+        "speedup_vs_dense": dense_ms / shared_ms,
+        "speedup_vs_per_layer_routing": per_layer_ms / shared_ms,
+        "note": "same-box baselines on the decode leg's caches; context, not the metric",
+    }
 
 
 def main():
@@ -158,6 +254,8 @@ def main():
     ap.add_argument("--workload", default="decode_128k_b8")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work in the baseline sample (0 = skip)")
+    ap.add_argument("--baseline-steps", type=int, default=5,
+                    help="timed steps of the dense and per-layer-routing baselines (0: skip)")
     ap.add_argument("--prefill-calls", type=int, default=10,
                     help="timed calls of the prefill-chunk routing leg (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -293,8 +391,11 @@ def main():
                            "frac": r_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "algorithmic_bytes_per_call": r_bytes},
     }
+    if args.baseline_steps > 0:
+        res["baselines"] = baselines(wl, Kc, Vc, q_all[total_steps - 1], N0 + total_steps, dev,
+                                     args.baseline_steps, ms_step)
     if args.prefill_calls > 0:
-        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev)
+        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget))
     if args.cpu_budget > 0:
         t = total_steps - 1
         res["cpu_baseline"] = cpu_baseline(wl, K_idx, Kc, Vc, q_idx_all[t], q_all[t],
