@@ -174,6 +174,30 @@ def prefill_routing(calls, dev, cpu_budget):
                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                         "algorithmic_flops_per_call": flops,
                         "what": "whole clsa_route call (threshold, filter, select)"}}
+    # sparse attention of the chunk over its routed lists, all 16 layers
+    # (query-major: every row gathers its own k rows per layer)
+    Kc, Vc = gen.gen_kv(wl, dev)
+    q = gen.gen_attn_query(wl, q_idx, 0, dev)
+    attn = clsa.prepare_sparse_attn(q, Kc, Vc, idx, counts)
+    attn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(2):
+        attn()
+    e1.record()
+    torch.cuda.synchronize()
+    a_ms = e0.elapsed_time(e1) / 2
+    row_bytes = wl.Hkv * wl.D * 2 * 2  # K and V of one position, all KV heads
+    gathered = wl.L * wl.B * wl.M * wl.k * row_bytes
+    unique = wl.L * wl.B * wl.n_ctx * row_bytes
+    res["attention"] = {
+        "ms_per_call": a_ms, "layers": wl.L,
+        "gathered_bytes": gathered, "achieved_GBs": gathered / (a_ms * 1e-3) / 1e9,
+        "hbm_frac": gathered / (a_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "unique_row_bytes": unique,
+        "unique_row_bound_ms": unique / (HBM_PEAK_GBS * 1e9) * 1e3,
+        "note": "query-major gather; a key-major kernel could approach the unique-row bound"}
+    del Kc, Vc, q, attn
     if cpu_budget > 0:
         res["cpu_baseline"] = prefill_cpu_baseline(wl, K_idx, q_idx, cpu_budget)
     return res
