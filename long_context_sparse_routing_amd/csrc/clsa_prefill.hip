@@ -16,9 +16,10 @@
 //                  threshold T.
 //   block_filter   the full score matrix in 32x32 MFMA tiles, keys as the A
 //                  operand and queries as B, so each lane owns one query
-//                  column; a workgroup keeps one key chunk in LDS and streams
-//                  query rows through it.  Keys scoring >= T are appended as
-//                  (score - T', position) to a segment of the lane's own.
+//                  column (two lanes per row, one per key half); a workgroup
+//                  keeps key chunks in LDS and streams query rows through
+//                  them.  Keys scoring >= T are appended as (score - T',
+//                  position) to the row's segment of the chunk.
 //   block_select   per row: the exact top-k among the candidates (lower
 //                  positions win ties), written in ascending order.  A row
 //                  whose threshold kept fewer than k keys, or more than the
@@ -36,7 +37,7 @@ constexpr int kSStride = 32;       // sampling stride of the threshold estimate
 constexpr int kStageKeys = 64;     // keys per filter step (two 32-key tiles)
 constexpr int kSelCap = 6144;      // candidates a select workgroup holds
 constexpr int kMaxK = 2048;
-constexpr int kMaxSegs = 2048;     // half-segments per row
+constexpr int kMaxSegs = 2048;     // candidate segments (key chunks) per row
 constexpr int64_t kMaxKeys = 524288;
 
 // Keys held in LDS by a filter workgroup at a time (64 KB of bf16 keys),
@@ -46,7 +47,10 @@ constexpr int64_t kMaxKeys = 524288;
 constexpr int sub_keys(int d) { return 32768 / d; }
 constexpr int kSubPerChunk = 4;
 constexpr int chunk_keys(int d) { return kSubPerChunk * sub_keys(d); }
-constexpr int kMaxRowsPerGroup = 1024;  // filter rows per workgroup: <= 2 pairs per wave
+// Filter rows per workgroup (one slab pair per wave): with 32 workgroups
+// per XCD this keeps the partly filled segment lines in flight (one per
+// row) within the XCD's 4 MB L2, so they fill before they are written back.
+constexpr int kMaxRowsPerGroup = 512;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -65,8 +69,8 @@ struct BlockArgs {
   int nchunks;             // key chunks per row
   int rows_pg;             // rows per filter workgroup (multiple of 64)
   float* thr;              // [R] filter threshold; -inf: every key, +inf: none
-  uint32_t* segcnt;        // [R][nchunks][2] candidates per half-segment
-  uint64_t* seg;           // [R][nchunks][2][kc/2]: position | (score - T') << 32
+  uint32_t* segcnt;        // [R][nchunks] candidates per segment
+  uint64_t* seg;           // [R][nchunks][kc]: position | (score - T') << 32
 };
 
 CLSA_DEV int64_t row_visible(const BlockArgs& a, int b, int m) {
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
 // bits of a step's 32 values per lane pack into one hit mask with one
 // v_alignbit each; lanes with hits spill their 32 values to LDS scratch and
 // up to four hits per lane per pass are appended as (dd, position) to the
-// lane's segment in HBM.  Rows that keep every key (threshold -inf) and
+// row's segment in HBM, the two lanes of a row one after the other.  Rows that keep every key (threshold -inf) and
 // tiles crossing a row's visibility limit take explicit compares instead.
 constexpr int kScrStride = 36;  // scratch words per lane (32 values, padded
                                 // so 16 consecutive lanes hit distinct banks)
@@ -406,8 +410,8 @@ struct SlabState {
   int32_t lim;      // keys visible to the lane's row
   int32_t lim_min;  // min over the slab (wave-uniform)
   bool sign_ok;     // every row of the slab has a finite threshold (uniform)
-  uint64_t* segp;   // the lane's half-segment in HBM
-  uint32_t gcnt;    // entries written there
+  uint64_t* segp;   // the row's segment of this chunk in HBM
+  uint32_t gcnt;    // entries written there (both lanes of the row)
 };
 
 // One step (two 32-key tiles) of one slab: the 32 values of this lane's
@@ -460,13 +464,27 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
 #pragma unroll
     for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q]];
     const uint32_t n = __popc(hits) - __popc(h);  // hits taken this pass (<= 4)
+    // lanes l and l+32 hold the same row: one stream, the upper lane after
+    // the lower one
+    const uint32_t n_pair = __shfl_xor(n, 32);
+    const uint32_t at = st.gcnt + (lane_id() >= 32 ? n_pair : 0u);
+    uint32_t pw[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if ((uint32_t)q < n) {
-        const int32_t pos = (jl0 + 2 * (idx[q] & 28)) | (idx[q] & 3);  // jl0 % 4 == 0
-        st.segp[st.gcnt + q] = ((uint64_t)__float_as_uint(dv[q]) << 32) | (uint32_t)pos;
-      }
-    st.gcnt += n;
+    for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)((jl0 + 2 * (idx[q] & 28)) | (idx[q] & 3));
+    // exactly the pass's n entries (the partner lane's follow them): pairs
+    // as 16-byte stores, an odd last one as 8 bytes
+    uint64_t* dst = st.segp + at;
+    if (n >= 2u)
+      reinterpret_cast<u32x4_t*>(dst)[0] =
+          u32x4_t{pw[0], __float_as_uint(dv[0]), pw[1], __float_as_uint(dv[1])};
+    else if (n == 1u)
+      dst[0] = ((uint64_t)__float_as_uint(dv[0]) << 32) | pw[0];
+    if (n == 4u)
+      reinterpret_cast<u32x4_t*>(dst)[1] =
+          u32x4_t{pw[2], __float_as_uint(dv[2]), pw[3], __float_as_uint(dv[3])};
+    else if (n == 3u)
+      dst[2] = ((uint64_t)__float_as_uint(dv[2]) << 32) | pw[2];
+    st.gcnt += n + n_pair;
     hits = h;
   }
 }
@@ -490,8 +508,8 @@ CLSA_DEV void load_pair(const BlockArgs& a, int b, int p0, int ch, bf16x8_t (&qb
     st[blk].lim = ok ? (int32_t)row_visible(a, b, m) : 0;
     st[blk].lim_min = (m0 + 31 < a.M) ? (int32_t)row_visible(a, b, m0) : 0;
     st[blk].sign_ok = __ballot(all) == 0;
-    const size_t sg = (((size_t)b * a.M + (ok ? m : 0)) * a.nchunks + ch) * 2 + lane / 32;
-    st[blk].segp = a.seg + sg * (size_t)(a.kc / 2);
+    const size_t sg = ((size_t)b * a.M + (ok ? m : 0)) * a.nchunks + ch;
+    st[blk].segp = a.seg + sg * (size_t)a.kc;
     st[blk].gcnt = 0;
   }
 }
@@ -603,7 +621,7 @@ __global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int m = p0 + blk * 32 + lane % 32;
-      if (m < r_hi) a.segcnt[(((size_t)b * a.M + m) * a.nchunks + ch) * 2 + lane / 32] = gcnt[pp][blk];
+      if (m < r_hi && lane < 32) a.segcnt[((size_t)b * a.M + m) * a.nchunks + ch] = gcnt[pp][blk];
     }
   }
 }
@@ -769,8 +787,8 @@ CLSA_DEV uint32_t block_excl_scan_arr(const uint32_t* in, uint32_t* out, int n, 
   return run;
 }
 
-// One workgroup per row.  Each thread holds a contiguous run of at most
-// kPerT candidates in registers; the row's selection is marked in a bitmap
+// One workgroup per row.  Each thread holds at most kPerT candidates in
+// registers (every kNT-th one); the row's selection is marked in a bitmap
 // over its key positions (dynamic LDS, 1024 bits per key chunk) and written
 // out in position order from a popcount prefix over the bitmap's words.
 constexpr int kPerT = kSelCap / kNT;
@@ -795,8 +813,8 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
     return;
   }
 
-  // offsets of the row's half-segments (key chunk c: segments 2c and 2c+1)
-  const int nseg = 2 * a.nchunks;
+  // offsets of the row's segments (one per key chunk)
+  const int nseg = a.nchunks;
   const uint32_t n_c = block_excl_scan_arr(a.segcnt + (size_t)r * nseg, segoff, nseg, S.tmp, S.bc);
   if (tid == 0) segoff[nseg] = n_c;
   __syncthreads();
@@ -806,29 +824,26 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
     return;
   }
 
-  // candidates [i0, i0 + cnt): locate each one's segment first (one binary
-  // search, then a forward walk), then issue all loads at once
-  const uint32_t per = (n_c + kNT - 1) / kNT;
-  const uint32_t i0 = (uint32_t)tid * per;
-  const int cnt = i0 < n_c ? (int)(n_c - i0 < per ? n_c - i0 : per) : 0;
+  // thread t holds candidates t, t + kNT, ...: a wave's loads cover
+  // consecutive entries (coalesced).  Each element's segment is found by an
+  // independent binary search over the offsets, so the searches overlap.
+  const int cnt = (int)((n_c + kNT - 1 - (uint32_t)tid) / kNT);  // elements of this thread
   uint32_t key[kPerT], pos[kPerT];
   {
-    int lo = 0, hi = nseg;  // segoff[lo] <= i0 < segoff[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (segoff[mid] <= i0) lo = mid;
-      else hi = mid;
-    }
+    const uint32_t half = (uint32_t)a.kc;  // segment capacity
     uint32_t off[kPerT];
-    const uint32_t half = (uint32_t)a.kc / 2;
-    int sg = lo;
 #pragma unroll
-    for (int u = 0; u < kPerT; ++u)
-      if (u < cnt) {
-        const uint32_t i = i0 + u;
-        while (segoff[sg + 1] <= i) ++sg;
-        off[u] = (uint32_t)sg * half + (i - segoff[sg]);
-      }
+    for (int u = 0; u < kPerT; ++u) {
+      const uint32_t i = (uint32_t)(u * kNT + tid);
+      int lo = 0, hi = nseg;  // segoff[lo] <= i < segoff[hi]
+      if (u < cnt)
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (segoff[mid] <= i) lo = mid;
+          else hi = mid;
+        }
+      off[u] = (uint32_t)lo * half + (i - segoff[lo]);
+    }
     const uint64_t* rowseg = a.seg + (size_t)r * nseg * half;
     uint64_t e[kPerT];
 #pragma unroll
@@ -936,7 +951,7 @@ BlockLayout block_layout(int64_t R, int d, int64_t n_cap) {
   L.nchunks = (int)ceil_div64(n_cap, L.kc);
   size_t o = 0;
   L.o_thr = o; o = align_up(o + (size_t)R * 4, 256);
-  L.o_cnt = o; o = align_up(o + (size_t)R * L.nchunks * 2 * 4, 256);
+  L.o_cnt = o; o = align_up(o + (size_t)R * L.nchunks * 4, 256);
   L.o_seg = o; o = align_up(o + (size_t)R * L.nchunks * L.kc * 8, 256);
   L.total = o;
   return L;
@@ -948,7 +963,7 @@ BlockLayout block_layout(int64_t R, int d, int64_t n_cap) {
 bool block_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt) {
   if (dt != CLSA_BF16 || M < 64 || k > kMaxK) return false;
   if (d != 32 && d != 64 && d != 128) return false;
-  return n_cap <= kMaxKeys && 2 * ceil_div64(n_cap, chunk_keys(d)) <= kMaxSegs;
+  return n_cap <= kMaxKeys && ceil_div64(n_cap, chunk_keys(d)) <= kMaxSegs;
 }
 
 size_t block_route_workspace(int B, int M, int d, int64_t n_cap) {
