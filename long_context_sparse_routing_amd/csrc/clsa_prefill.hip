@@ -439,7 +439,7 @@ CLSA_DEV uint32_t stage_hits(const f32x16_t& x0, const f32x16_t& x1, const SlabS
 }
 
 // Spill the step's values of lanes with hits to scratch, then append the
-// hits (dd, position) to the lane's segment, up to four per lane per pass
+// hits (dd, position) to the row's segment, up to four per lane per pass
 // so that each pass waits on LDS once.
 CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, SlabState& st,
                          int32_t jl0, float* scr) {
