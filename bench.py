@@ -270,6 +270,99 @@ def baselines(wl, Kc, Vc, q, n, dev, steps, shared_ms):
     }
 
 
+def _event_ms(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def threshold_step(dev, reps):
+    """Half-space selection at 128K: 16 sequences, d_idx 128, per-sequence
+    tau set so that 256 .. 8192 keys qualify (Louver summary, section on the
+    half-space reduction), then attention over those lists in 16 layers."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+    wl = gen.WORKLOADS["threshold_128k_b16"]
+    # input preparation: tau from fp64 scores on the host
+    K_cpu, q_cpu, tau = gen.gen_threshold_inputs(wl, lambda qq, KK: KK @ qq)
+    K_idx, q_idx, tau_d = K_cpu.to(dev), q_cpu.to(dev), tau.to(dev)
+    cap = 8192
+    route = clsa.prepare_route_threshold(q_idx, K_idx, tau_d, cap)
+    idx, counts = route()
+    Kc, Vc = gen.gen_kv(wl, dev)
+    q = gen.gen_attn_query(wl, q_idx, 0, dev)
+    attn = clsa.prepare_sparse_attn(q, Kc, Vc, idx, counts)
+    route_ms = _event_ms(route, reps)
+    attn_ms = _event_ms(attn, reps)
+    step_ms = _event_ms(lambda: (route(), attn()), reps)
+    sel = int(counts.sum())
+    scan = wl.B * wl.n_ctx * wl.d * 2
+    gather = sel * wl.L * wl.Hkv * wl.D * 2 * 2
+    step_bytes = scan + gather + 2 * q.numel() * 2
+    del Kc, Vc, q, attn, route, K_idx
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "sequences": wl.B, "selected_total": sel,
+            "route_call_ms": route_ms, "attn_call_ms": attn_ms, "ms_per_step": step_ms,
+            "tokens_per_s": wl.B / (step_ms * 1e-3),
+            "route_roofline": {"bound": "hbm", "achieved": scan / (route_ms * 1e-3) / 1e9,
+                               "unit": "GB/s", "frac": scan / (route_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                               "algorithmic_bytes_per_call": scan},
+            "step_hbm_frac": step_bytes / (step_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+
+
+def decode_32k_step(dev, steps):
+    """One sequence at 32K context: append + route + attention in 16 layers,
+    the single-sequence case where attention lists are split across
+    workgroups and merged."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+    base = gen.WORKLOADS["decode_32k"]
+    wl = base.with_(n_cap=base.n_ctx + steps + 2)
+    N0 = wl.n_ctx
+    K_idx, u, _ = gen.gen_routing_keys(wl, dev)
+    Kc, Vc = gen.gen_kv(wl, dev)
+    T = steps + 2
+    new_kidx, new_k, new_v = gen.gen_append_rows(wl, T, dev)
+    qi = [gen.gen_routing_query(wl, u, t, dev) for t in range(T)]
+    qa = [gen.gen_attn_query(wl, qi[t], t, dev) for t in range(T)]
+    nctx = torch.tensor([[N0 + t + 1] for t in range(T)], dtype=torch.int32, device=dev)
+    idx = torch.empty((1, 1, wl.k), dtype=torch.int32, device=dev)
+    counts = torch.empty((1, 1), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.L, 1, 1, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    calls = [(clsa.prepare_kv_append(nctx[t] - 1, new_kidx[t], K_idx, new_k[t], Kc, new_v[t], Vc),
+              clsa.prepare_route(qi[t], K_idx, wl.k, n_ctx=nctx[t], idx=idx, counts=counts),
+              clsa.prepare_sparse_attn(qa[t], Kc, Vc, idx, counts, out=out)) for t in range(T)]
+    for t in range(2):
+        for c in calls[t]:
+            c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for t in range(2, T):
+        for c in calls[t]:
+            c()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n_mid = N0 + 2 + steps // 2
+    step_bytes = (n_mid * wl.d * 2 + wl.L * wl.k * wl.Hkv * wl.D * 2 * 2
+                  + 2 * wl.L * wl.Hq * wl.D * 2)
+    del Kc, Vc, K_idx, calls
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "steps": steps, "ms_per_step": ms,
+            "tokens_per_s": 1.0 / (ms * 1e-3), "bytes_per_step": step_bytes,
+            "step_hbm_frac": step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +373,8 @@ def main():
                     help="seconds of CPU oracle work in the baseline sample (0 = skip)")
     ap.add_argument("--baseline-steps", type=int, default=5,
                     help="timed steps of the dense and per-layer-routing baselines (0: skip)")
+    ap.add_argument("--other-configs", type=int, default=1,
+                    help="also time the threshold (16 x 128K) and 32K decode configurations")
     ap.add_argument("--prefill-calls", type=int, default=10,
                     help="timed calls of the prefill-chunk routing leg (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -418,12 +513,18 @@ def main():
     if args.baseline_steps > 0:
         res["baselines"] = baselines(wl, Kc, Vc, q_all[total_steps - 1], N0 + total_steps, dev,
                                      args.baseline_steps, ms_step)
-    if args.prefill_calls > 0:
-        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget))
     if args.cpu_budget > 0:
         t = total_steps - 1
         res["cpu_baseline"] = cpu_baseline(wl, K_idx, Kc, Vc, q_idx_all[t], q_all[t],
                                            N0 + t + 1, args.cpu_budget)
+    # the decode caches are released before the other configurations
+    del Kc, Vc, appends, routes, attns, q_all, q_idx_all, new_kidx, new_k, new_v, K_idx
+    torch.cuda.empty_cache()
+    if args.other_configs:
+        res["threshold_128k_b16"] = threshold_step(dev, 5)
+        res["decode_32k"] = decode_32k_step(dev, 64)
+    if args.prefill_calls > 0:
+        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget))
     print(json.dumps(res), flush=True)
 
 

@@ -10,6 +10,7 @@ from .binding import (  # noqa: F401
     load_library,
     prepare_kv_append,
     prepare_route,
+    prepare_route_threshold,
     prepare_sparse_attn,
     route,
     route_threshold,

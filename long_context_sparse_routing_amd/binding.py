@@ -169,11 +169,11 @@ def route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int, n_ctx: torch.Tensor 
     return prepare_route(q_idx, K_idx, k, n_ctx, q_pos0, cap, idx, counts, ws, stream)()
 
 
-def route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor, cap: int,
-                    n_ctx: torch.Tensor | None = None, q_pos0: int = -1,
-                    idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
-                    ws: torch.Tensor | None = None, stream=None):
-    """clsa_route_threshold: tau [B, M] float32 -> (idx [B, M, cap], true counts [B, M])."""
+def prepare_route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor,
+                            cap: int, n_ctx: torch.Tensor | None = None, q_pos0: int = -1,
+                            idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                            ws: torch.Tensor | None = None, stream=None) -> Prepared:
+    """clsa_route_threshold, marshalled: calling the result returns (idx, counts)."""
     lib = load_library()
     B, M, d = q_idx.shape
     n_cap = K_idx.shape[1]
@@ -188,12 +188,20 @@ def route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor,
     dt = _dt(q_idx)
     need = lib.clsa_route_threshold_workspace_size(B, M, d, n_cap, cap, dt)
     ws = _workspace(need, dev, ws)
-    st = lib.clsa_route_threshold(_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0,
-                                  _ptr(tau), dt, _ptr(idx), _ptr(counts), cap, _ptr(ws),
-                                  ws.numel() * ws.element_size(), _stream(stream))
-    if st != 0:
-        raise ClsaError("clsa_route_threshold", st)
-    return idx, counts
+    args = (_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0, _ptr(tau), dt,
+            _ptr(idx), _ptr(counts), cap, _ptr(ws), ws.numel() * ws.element_size(),
+            _stream(stream))
+    return Prepared("clsa_route_threshold", lib.clsa_route_threshold, args, (idx, counts),
+                    (q_idx, K_idx, tau, n_ctx, idx, counts, ws))
+
+
+def route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor, cap: int,
+                    n_ctx: torch.Tensor | None = None, q_pos0: int = -1,
+                    idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                    ws: torch.Tensor | None = None, stream=None):
+    """clsa_route_threshold: tau [B, M] float32 -> (idx [B, M, cap], true counts [B, M])."""
+    return prepare_route_threshold(q_idx, K_idx, tau, cap, n_ctx, q_pos0, idx, counts, ws,
+                                   stream)()
 
 
 def _layers(x) -> list:
