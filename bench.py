@@ -142,9 +142,10 @@ def prefill_cpu_baseline(wl, K_idx, q_idx, budget_s):
                        f"~{wl.n_ctx} keys, exact top-{wl.k}); NumPy BLAS threads={blas_threads}")}
 
 
-def prefill_routing(calls, dev, cpu_budget):
+def prefill_routing(calls, dev, cpu_budget, with_attention=True):
     """Route one prefill chunk (4096 rows at positions 126976.., 128K keys,
-    d_idx 64, k 2048, causal) `calls` times; the score matrix runs on MFMA."""
+    d_idx 64, k 2048, causal) `calls` times; the score matrix runs on MFMA.
+    With `with_attention`, also time the chunk's sparse attention."""
     import torch
     from long_context_sparse_routing_amd import binding as clsa
     from long_context_sparse_routing_amd import inputs as gen
@@ -162,6 +163,9 @@ def prefill_routing(calls, dev, cpu_budget):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / calls
+    # K_idx (16 MiB) stays cache-resident across back-to-back calls: the same
+    # calls again, each timed alone after evicting the last-level cache
+    cold_us = _mall_cold_ms([call] * calls) * 1e3
     idx, counts = call.result
     assert int(counts.min()) == wl.k and int(counts.max()) == wl.k
     n_scores = wl.B * sum(min(wl.n_ctx, wl.q_pos0 + m + 1) for m in range(wl.M))
@@ -173,7 +177,14 @@ def prefill_routing(calls, dev, cpu_budget):
            "roofline": {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": tflops / MFMA_BF16_PEAK_TFLOPS,
                         "algorithmic_flops_per_call": flops,
-                        "what": "whole clsa_route call (threshold, filter, select)"}}
+                        "what": "whole clsa_route call (threshold, filter, select)"},
+           "mall_cold": {"us_per_call": cold_us,
+                         "frac": flops / (cold_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                         "how": "each call timed alone after a 512 MiB write"}}
+    if not with_attention:
+        if cpu_budget > 0:
+            res["cpu_baseline"] = prefill_cpu_baseline(wl, K_idx, q_idx, cpu_budget)
+        return res
     # sparse attention of the chunk over its routed lists, all 16 layers
     # (query-major: every row gathers its own k rows per layer)
     Kc, Vc = gen.gen_kv(wl, dev)
@@ -283,6 +294,25 @@ def _event_ms(fn, reps):
     return e0.elapsed_time(e1) / reps
 
 
+def _mall_cold_ms(calls):
+    """Time each call on its own with events, after writing a 512 MiB buffer
+    (outside the timed region) so that nothing it reads is still resident
+    in the 256 MB last-level cache.  Returns the mean per call in ms."""
+    import torch
+    scrub = torch.empty(1 << 28, dtype=torch.int16, device="cuda")
+    evs = []
+    for i, fn in enumerate(calls):
+        scrub.fill_(i & 0x7FFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        evs.append((e0, e1))
+    torch.cuda.synchronize()
+    del scrub
+    return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+
 def threshold_step(dev, reps):
     """Half-space selection at 128K: 16 sequences, d_idx 128, per-sequence
     tau set so that 256 .. 8192 keys qualify (Louver summary, section on the
@@ -353,6 +383,9 @@ def decode_32k_step(dev, steps):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # the 32K working set (~139 MB) fits the last-level cache: the same
+    # steps again, each timed alone after evicting it
+    cold_ms = _mall_cold_ms([lambda c=c: [f() for f in c] for c in calls[2:]])
     n_mid = N0 + 2 + steps // 2
     step_bytes = (n_mid * wl.d * 2 + wl.L * wl.k * wl.Hkv * wl.D * 2 * 2
                   + 2 * wl.L * wl.Hq * wl.D * 2)
@@ -360,7 +393,10 @@ def decode_32k_step(dev, steps):
     torch.cuda.empty_cache()
     return {"workload": wl.name, "steps": steps, "ms_per_step": ms,
             "tokens_per_s": 1.0 / (ms * 1e-3), "bytes_per_step": step_bytes,
-            "step_hbm_frac": step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+            "step_hbm_frac": step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+            "mall_cold": {"ms_per_step": cold_ms,
+                          "step_hbm_frac": step_bytes / (cold_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                          "how": "each step timed alone after a 512 MiB write"}}
 
 
 def main():
@@ -377,6 +413,8 @@ def main():
                     help="also time the threshold (16 x 128K) and 32K decode configurations")
     ap.add_argument("--prefill-calls", type=int, default=10,
                     help="timed calls of the prefill-chunk routing leg (0: skip)")
+    ap.add_argument("--prefill-attention", type=int, default=1,
+                    help="also time the prefill chunk's sparse attention (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
@@ -524,7 +562,8 @@ def main():
         res["threshold_128k_b16"] = threshold_step(dev, 5)
         res["decode_32k"] = decode_32k_step(dev, 64)
     if args.prefill_calls > 0:
-        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget))
+        res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget),
+                                                 bool(args.prefill_attention))
     print(json.dumps(res), flush=True)
 
 

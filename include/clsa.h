@@ -96,6 +96,13 @@ const char* clsa_status_string(int status);
  * every key, so the selection and tie rule are the same on both paths; the
  * scores themselves may differ from the one-query path in the last bits
  * (fp32 summation order).
+ * Other bf16 rows with k <= 2048 and n_cap <= 512K (decode: one query per
+ * sequence) first score up to 4096 evenly spaced keys for a per-row lower
+ * bound of the k-th score, then stream every visible key once and keep only
+ * those at or above it; the workspace holds about 56 KB per row whatever
+ * n_cap is.  A row whose bound keeps fewer than k keys, or more than 6144,
+ * is redone exactly (much slower, results unchanged).  Other rows (fp32, or
+ * k > 2048) keep every key's score in the workspace (12 bytes per key).
  * Errors: CLSA_ERR_INVALID (null pointer, B/M/k < 1, d unsupported,
  * n_cap < 1, cap < k, B*M*n_cap too large), CLSA_ERR_UNSUPPORTED_DTYPE,
  * CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.

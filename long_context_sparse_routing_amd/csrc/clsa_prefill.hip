@@ -199,11 +199,6 @@ struct SelScratch {  // LDS scratch of the block selects
   uint32_t bc[8];
 };
 
-// inverse of score_key
-CLSA_DEV float key_to_float(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
 // ------------------------------------------------------------------ thresh
 // One workgroup per 16 query rows.  Scores against every a.ss-th key come
 // from v_mfma_f32_16x16x32_bf16 and stay in LDS as the top 16 bits of their
@@ -294,9 +289,7 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
       continue;
     }
     const int ns = (int)((n_vis + a.ss - 1) / a.ss);  // visible samples
-    const float kappa = (float)k_eff * (float)ns / (float)n_vis;
-    const float sr = 2.0f + sqrtf(4.0f + kappa);
-    const int64_t rho = (int64_t)ceilf(sr * sr);
+    const int rho = sample_rank(n_vis, k_eff, ns);
     if (rho > ns) {  // too few samples to bound the k-th score: keep every key
       if (lane == 0) a.thr[r] = -INFINITY;
       continue;
@@ -304,77 +297,93 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
     // the row's samples in registers (lane l: samples l, l+64, ...)
     const uint16_t* row = sk[rl];
     uint32_t v[kThrNs / kWave];
-    uint32_t lo = 0xffffu, hi = 0u;
 #pragma unroll
     for (int u = 0; u < kThrNs / kWave; ++u) {
       const int i = lane + u * kWave;
       v[u] = i < ns ? row[i] : 0u;
-      if (i < ns) {
-        lo = v[u] < lo ? v[u] : lo;
-        hi = v[u] > hi ? v[u] : hi;
-      }
     }
-#pragma unroll
-    for (int mm = 32; mm >= 1; mm >>= 1) {
-      const uint32_t l2 = __shfl_xor(lo, mm), h2 = __shfl_xor(hi, mm);
-      lo = l2 < lo ? l2 : lo;
-      hi = h2 > hi ? h2 : hi;
-    }
-    // one histogram over the row's actual key range; the threshold is the
-    // lower edge of the bin holding the rho-th largest sample (<= it)
-    const uint32_t range = hi - lo;
-    const int shift = range < kThrBins ? 0 : (32 - __clz(range)) - 10;
-#pragma unroll
-    for (int i = 0; i < kThrBins / kWave; ++i) h[lane + kWave * i] = 0u;
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int u = 0; u < kThrNs / kWave; ++u)
-      if (lane + u * kWave < ns) atomicAdd(&h[(v[u] - lo) >> shift], 1u);
-    __builtin_amdgcn_wave_barrier();
-    // bins in descending order: lane l holds bins 1023-16l .. 1008-16l
-    uint32_t c[kThrBins / kWave], sum = 0;
-#pragma unroll
-    for (int i = 0; i < kThrBins / kWave; ++i) {
-      c[i] = h[kThrBins - 1 - (kThrBins / kWave) * lane - i];
-      sum += c[i];
-    }
-    const uint32_t incl = wave_incl_scan(sum);
-    const bool mine = incl - sum < (uint32_t)rho && (uint32_t)rho <= incl;
-    uint32_t bin = 0, rin = 0;  // bin of the rho-th largest, its rank inside
-    if (mine) {
-      uint32_t acc = incl - sum;
-#pragma unroll
-      for (int i = 0; i < kThrBins / kWave; ++i) {
-        if (acc + c[i] >= (uint32_t)rho) {
-          bin = kThrBins - 1 - (kThrBins / kWave) * lane - i;
-          rin = (uint32_t)rho - acc;
-          break;
-        }
-        acc += c[i];
-      }
-    }
-    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-    bin = __shfl(bin, src);
-    rin = __shfl(rin, src);
-    uint32_t kth = lo + (bin << shift);  // 16-bit key of the rho-th largest
-    if (shift > 0) {
-      // second pass: the bin's 2^shift (<= 64) keys, exactly
-      __builtin_amdgcn_wave_barrier();
-      h[lane] = 0u;
-      __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int u = 0; u < kThrNs / kWave; ++u)
-        if (lane + u * kWave < ns && (v[u] - kth) < (1u << shift)) atomicAdd(&h[v[u] - kth], 1u);
-      __builtin_amdgcn_wave_barrier();
-      const uint32_t cc = lane < (1 << shift) ? h[(1 << shift) - 1 - lane] : 0u;  // descending
-      const uint32_t inc2 = wave_incl_scan(cc);
-      const bool mine2 = inc2 - cc < rin && rin <= inc2;
-      const int src2 = __ffsll((unsigned long long)__ballot(mine2)) - 1;
-      kth += (uint32_t)((1 << shift) - 1 - src2);
-    }
-    __builtin_amdgcn_wave_barrier();
+    const uint32_t kth =
+        wave_kth_u16(v, [&](int u) { return lane + u * kWave < ns; }, (uint32_t)rho, h);
     // smallest float of the 16-bit bucket: never above the sample
     if (lane == 0) a.thr[r] = key_to_float(kth << 16);
+  }
+}
+
+// Rows whose keys no other row shares (a decode step: one query per
+// sequence), sampled as row_plan says: ceil(ns / kNT) workgroups score the
+// samples on the matrix cores (one per thread) and store their 16-bit key
+// prefixes -- each wave's kRowTop largest when the plan is compact, else
+// all of them -- for the score pass, which ranks them (rank_row_samples).
+// The first workgroup of each row also zeroes the row's candidate count.
+constexpr int kRowNs = kRowSamples;
+constexpr int kRowSampleWG = kRowNs / kNT;  // one sample per thread
+
+template <int D>
+__global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
+  const int r = blockIdx.y, b = r / a.M, m = r % a.M;
+  const int lane = lane_id(), w = threadIdx.x / kWave;
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.segcnt[r] = 0u;  // the filter's candidate count
+  const int64_t n_vis = row_visible(a, b, m);
+  const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
+  if (k_eff >= n_vis) return;  // the select takes every visible key
+  const RowPlan p = row_plan(n_vis, k_eff);
+  const int s0 = blockIdx.x * kNT + w * kWave;  // the wave's 64 samples: 4 MFMA tiles
+  if (p.rho > p.ns || s0 >= p.ns) return;
+  uint16_t* row = samp + (size_t)r * kRowNs;
+
+  // A operand: the row's query in all 16 MFMA rows; B: 16 sampled keys, so
+  // lanes 0..15 receive the scores of their samples in accumulator value 0
+  bf16x8_t qa[D / 32], kb[4][D / 32];
+#pragma unroll
+  for (int st = 0; st < D / 32; ++st)
+    qa[st] = __builtin_bit_cast(
+        bf16x8_t, *reinterpret_cast<const u32x4_t*>(a.q + (size_t)r * D + 32 * st + 8 * (lane / 16)));
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int smp = s0 + u * 16 + lane % 16;
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st) {
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (smp < p.ns)
+        v = *reinterpret_cast<const u32x4_t*>(
+            a.K + ((size_t)b * a.n_cap + (size_t)((int64_t)smp * n_vis / p.ns)) * D + 32 * st +
+            8 * (lane / 16));
+      kb[u][st] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+  // lane l < 16 holds samples s0 + 16 u + l; samples past ns count as 0,
+  // below every real prefix
+  uint32_t key[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < D / 32; ++st)
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], kb[u][st], c, 0, 0, 0);
+    const int smp = s0 + u * 16 + lane;
+    key[u] = (lane < 16 && smp < p.ns) ? score_key(c[0]) >> 16 : 0u;
+  }
+  if (p.compact) {
+    // the wave's kRowTop largest: take the maximum, knock one copy out
+#pragma unroll
+    for (int t = 0; t < kRowTop; ++t) {
+      uint32_t mx = key[0];
+#pragma unroll
+      for (int u = 1; u < 4; ++u) mx = key[u] > mx ? key[u] : mx;
+      mx = wave_max_u32(mx);
+      const uint64_t has = __ballot(key[0] == mx || key[1] == mx || key[2] == mx || key[3] == mx);
+      if (lane == __ffsll((unsigned long long)has) - 1) {
+        bool gone = false;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (!gone && key[u] == mx) key[u] = 0u, gone = true;
+      }
+      if (lane == 0) row[(s0 / kWave) * kRowTop + t] = (uint16_t)mx;
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (lane < 16 && s0 + u * 16 + lane < p.ns) row[s0 + u * 16 + lane] = (uint16_t)key[u];
   }
 }
 
@@ -696,12 +705,8 @@ CLSA_DEV uint32_t kth_regs(const uint32_t (&k)[NPER], int cnt, uint32_t rank, Se
       lo = k[u] < lo ? k[u] : lo;
       hi = k[u] > hi ? k[u] : hi;
     }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t l2 = __shfl_xor(lo, m), h2 = __shfl_xor(hi, m);
-    lo = l2 < lo ? l2 : lo;
-    hi = h2 > hi ? h2 : hi;
-  }
+  lo = wave_min_u32(lo);
+  hi = wave_max_u32(hi);
   if (lane_id() == 0) S.lo[w] = lo, S.hi[w] = hi;
   __syncthreads();
 #pragma unroll
@@ -789,14 +794,25 @@ CLSA_DEV uint32_t block_excl_scan_arr(const uint32_t* in, uint32_t* out, int n, 
 
 // One workgroup per row.  Each thread holds at most kPerT candidates in
 // registers (every kNT-th one); the row's selection is marked in a bitmap
-// over its key positions (dynamic LDS, 1024 bits per key chunk) and written
+// over its key positions (dynamic LDS, one bit per position) and written
 // out in position order from a popcount prefix over the bitmap's words.
 constexpr int kPerT = kSelCap / kNT;
 
-template <int D>
+// Bitmap words each select thread owns (contiguous, a multiple of 4 so they
+// are read 16 bytes at a time); the bitmap covers kNT times that many words.
+__host__ __device__ inline int select_words_per_thread(int64_t n_cap) {
+  const int64_t w = ceil_div64(ceil_div64(n_cap, 32), kNT);
+  return (int)((w + 3) / 4 * 4);
+}
+
+// CONTIG: the row's candidates are one contiguous list of segcnt[r] entries
+// at seg + r * kSelCap (the decode-row filter); otherwise a.nchunks
+// segments of a.kc entries each, segcnt[r][c] used.
+template <int D, bool CONTIG>
 __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
-  extern __shared__ uint32_t bitmap[];  // ceil(n_cap / 32) words
-  __shared__ uint32_t segoff[kMaxSegs + 1];
+  extern __shared__ u32x4_t bitmap4[];  // kNT * select_words_per_thread(n_cap) words
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(bitmap4);
+  __shared__ uint32_t segoff[CONTIG ? 1 : kMaxSegs + 1];
   __shared__ SelScratch S;
   __shared__ uint32_t wcnt[kNT / kWave];
 
@@ -814,10 +830,15 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   }
 
   // offsets of the row's segments (one per key chunk)
-  const int nseg = a.nchunks;
-  const uint32_t n_c = block_excl_scan_arr(a.segcnt + (size_t)r * nseg, segoff, nseg, S.tmp, S.bc);
-  if (tid == 0) segoff[nseg] = n_c;
-  __syncthreads();
+  const int nseg = CONTIG ? 1 : a.nchunks;
+  uint32_t n_c;
+  if constexpr (CONTIG) {
+    n_c = a.segcnt[r];  // the true count, even past the list's capacity
+  } else {
+    n_c = block_excl_scan_arr(a.segcnt + (size_t)r * nseg, segoff, nseg, S.tmp, S.bc);
+    if (tid == 0) segoff[nseg] = n_c;
+    __syncthreads();
+  }
 
   if (n_c < (uint32_t)k_eff || n_c > (uint32_t)kSelCap) {
     exact_rescan<D>(a, b, m, n_vis, k_eff, out, S.h, S.tmp, S.bc, wcnt);
@@ -825,25 +846,43 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   }
 
   // thread t holds candidates t, t + kNT, ...: a wave's loads cover
-  // consecutive entries (coalesced).  Each element's segment is found by an
-  // independent binary search over the offsets, so the searches overlap.
+  // consecutive entries (coalesced).  Each element's segment (the last one
+  // starting at or before it) is found by binary lifting over the offsets,
+  // all of the thread's searches in step so that each step waits on LDS once.
   const int cnt = (int)((n_c + kNT - 1 - (uint32_t)tid) / kNT);  // elements of this thread
   uint32_t key[kPerT], pos[kPerT];
-  {
-    const uint32_t half = (uint32_t)a.kc;  // segment capacity
-    uint32_t off[kPerT];
+  if constexpr (CONTIG) {
+    const uint64_t* row = a.seg + (size_t)r * kSelCap;
+    uint64_t e[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) e[u] = u < cnt ? row[u * kNT + tid] : 0ull;
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) {
-      const uint32_t i = (uint32_t)(u * kNT + tid);
-      int lo = 0, hi = nseg;  // segoff[lo] <= i < segoff[hi]
-      if (u < cnt)
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (segoff[mid] <= i) lo = mid;
-          else hi = mid;
-        }
-      off[u] = (uint32_t)lo * half + (i - segoff[lo]);
+      key[u] = score_key(__uint_as_float((uint32_t)(e[u] >> 32)));
+      pos[u] = (uint32_t)e[u];
     }
+  } else {
+    const uint32_t half = (uint32_t)a.kc;  // segment capacity
+    int lo[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) lo[u] = 0;
+    int step = 1;
+    while (2 * step < nseg) step *= 2;
+    for (; step > 0; step >>= 1) {
+      uint32_t sv[kPerT];
+#pragma unroll
+      for (int u = 0; u < kPerT; ++u) {
+        const int t = lo[u] + step;
+        sv[u] = segoff[t < nseg ? t : nseg];  // segoff[nseg] = n_c: never taken
+      }
+#pragma unroll
+      for (int u = 0; u < kPerT; ++u)
+        lo[u] = sv[u] <= (uint32_t)(u * kNT + tid) ? lo[u] + step : lo[u];
+    }
+    uint32_t off[kPerT];
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u)
+      off[u] = (uint32_t)lo[u] * half + ((uint32_t)(u * kNT + tid) - segoff[lo[u]]);
     const uint64_t* rowseg = a.seg + (size_t)r * nseg * half;
     uint64_t e[kPerT];
 #pragma unroll
@@ -860,11 +899,10 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
 
   // mark the selection: keys above kstar, and of the keys equal to it the
   // `left` lowest positions
-  const int nwords = (int)((a.n_cap + 31) / 32);
-  for (int i = tid; i < nwords; i += kNT) bitmap[i] = 0u;
-  __syncthreads();
-  const int wpt = (nwords + kNT - 1) / kNT;  // bitmap words per thread, contiguous
+  const int wpt = select_words_per_thread(a.n_cap);  // bitmap words per thread, contiguous
   const int w0 = tid * wpt;
+  for (int i = w0; i < w0 + wpt; i += 4) bitmap4[i / 4] = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
   if (left == eq_total) {
 #pragma unroll
     for (int u = 0; u < kPerT; ++u)
@@ -893,9 +931,9 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
       if (u < cnt && key[u] == kstar) atomicOr(&bitmap[pos[u] >> 5], 1u << (pos[u] & 31));
     __syncthreads();
     uint32_t mine = 0;
-    for (int i = w0; i < w0 + wpt && i < nwords; ++i) mine += __popc(bitmap[i]);
+    for (int i = w0; i < w0 + wpt; ++i) mine += __popc(bitmap[i]);
     uint32_t rank = block_incl_scan<kNT>(mine, S.tmp) - mine;
-    for (int i = w0; i < w0 + wpt && i < nwords; ++i) {
+    for (int i = w0; i < w0 + wpt; ++i) {
       uint32_t word = bitmap[i];
       for (uint32_t rest = word; rest != 0u; rest &= rest - 1u) {
         if (rank >= left) word &= ~(rest & (0u - rest));
@@ -910,16 +948,23 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   }
   __syncthreads();
 
-  // emit in position order
+  // emit in position order, the thread's words read 16 bytes at a time
   uint32_t mine = 0;
-  for (int i = w0; i < w0 + wpt && i < nwords; ++i) mine += __popc(bitmap[i]);
+  for (int i = w0; i < w0 + wpt; i += 4) {
+    const u32x4_t x = bitmap4[i / 4];
+    mine += __popc(x[0]) + __popc(x[1]) + __popc(x[2]) + __popc(x[3]);
+  }
   uint32_t slot = block_incl_scan<kNT>(mine, S.tmp) - mine;
-  for (int i = w0; i < w0 + wpt && i < nwords; ++i) {
-    uint32_t word = bitmap[i];
-    while (word != 0u) {
-      const int bit = __builtin_ctz(word);
-      out[slot++] = (int32_t)((uint32_t)i * 32u + (uint32_t)bit);
-      word &= word - 1u;
+  for (int i = w0; i < w0 + wpt; i += 4) {
+    const u32x4_t x = bitmap4[i / 4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t word = x[e];
+      while (word != 0u) {
+        const int bit = __builtin_ctz(word);
+        out[slot++] = (int32_t)((uint32_t)(i + e) * 32u + (uint32_t)bit);
+        word &= word - 1u;
+      }
     }
   }
 }
@@ -933,8 +978,8 @@ void launch_block(const BlockArgs& a, hipStream_t s) {
                      dim3((unsigned)a.nchunks, (unsigned)((a.M + a.rows_pg - 1) / a.rows_pg),
                           (unsigned)a.B),
                      dim3(kFT), 0, s, a);
-  hipLaunchKernelGGL(block_select<D>, dim3((unsigned)R), dim3(kNT),
-                     (size_t)((a.n_cap + 31) / 32) * sizeof(uint32_t), s, a);
+  hipLaunchKernelGGL((block_select<D, false>), dim3((unsigned)R), dim3(kNT),
+                     (size_t)select_words_per_thread(a.n_cap) * kNT * sizeof(uint32_t), s, a);
 }
 
 struct BlockLayout {
@@ -1004,6 +1049,60 @@ int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64
   else if (d == 64) launch_block<64>(a, s);
   else launch_block<128>(a, s);
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
+}
+
+// Few query rows per sequence (decode): the threshold and the select of
+// block routing around a streaming score pass (clsa_route.hip) that writes
+// the candidates of each key chunk into that chunk's segment.
+bool seg_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt) {
+  if (dt != CLSA_BF16 || k > kMaxK) return false;
+  if (d != 32 && d != 64 && d != 128) return false;
+  return n_cap <= kMaxKeys;
+}
+
+namespace {
+BlockArgs seg_args(const void* q_idx, const void* K_idx, int B, int M, int64_t n_cap,
+                   const int32_t* n_ctx, int64_t q_pos0, int k) {
+  BlockArgs a{};
+  a.q = static_cast<const uint16_t*>(q_idx);
+  a.K = static_cast<const uint16_t*>(K_idx);
+  a.n_ctx = n_ctx;
+  a.n_cap = n_cap;
+  a.q_pos0 = q_pos0 < 0 ? -1 : q_pos0;
+  a.B = B;
+  a.M = M;
+  a.k = k;
+  return a;
+}
+}  // namespace
+
+void seg_route_sample(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                      const int32_t* n_ctx, int64_t q_pos0, int k, uint16_t* samp,
+                      uint32_t* rowcnt, hipStream_t s) {
+  BlockArgs a = seg_args(q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, k);
+  a.segcnt = rowcnt;
+  const dim3 grid((unsigned)kRowSampleWG, (unsigned)(B * M));
+  if (d == 32) hipLaunchKernelGGL(row_sample<32>, grid, dim3(kNT), 0, s, a, samp);
+  else if (d == 64) hipLaunchKernelGGL(row_sample<64>, grid, dim3(kNT), 0, s, a, samp);
+  else hipLaunchKernelGGL(row_sample<128>, grid, dim3(kNT), 0, s, a, samp);
+}
+
+int seg_route_list_cap() { return kSelCap; }
+
+void seg_route_select(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                      const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
+                      int cap, uint32_t* rowcnt, uint64_t* cand, hipStream_t s) {
+  BlockArgs a = seg_args(q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, k);
+  a.idx = idx;
+  a.counts = counts;
+  a.cap = cap;
+  a.segcnt = rowcnt;
+  a.seg = cand;
+  const dim3 grid((unsigned)(B * M));
+  const size_t lds = (size_t)select_words_per_thread(n_cap) * kNT * sizeof(uint32_t);
+  if (d == 32) hipLaunchKernelGGL((block_select<32, true>), grid, dim3(kNT), lds, s, a);
+  else if (d == 64) hipLaunchKernelGGL((block_select<64, true>), grid, dim3(kNT), lds, s, a);
+  else hipLaunchKernelGGL((block_select<128, true>), grid, dim3(kNT), lds, s, a);
 }
 
 }  // namespace clsa

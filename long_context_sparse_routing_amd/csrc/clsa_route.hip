@@ -33,9 +33,19 @@
 //   route_compact  writes the selected positions of its chunk in ascending
 //                  order with wave ballots from the chunk's offset; pads
 //                  with -1 and sets counts.
+// bf16 top-k with k <= 2048 over at most 512K keys takes a shorter path
+// instead: row_sample (clsa_prefill.hip) scores up to 4096 evenly spaced
+// keys of each row; route_score in filter mode ranks them (every workgroup
+// for itself) for a lower bound T of the row's k-th largest score and
+// appends the chunk's keys scoring >= T as (position, score) to the row's
+// candidate list;
+// block_select (clsa_prefill.hip) takes the exact top-k of those candidates.
+// Scores are the same in both paths.
 #include "clsa_common.h"
 
 namespace clsa {
+int seg_route_list_cap();  // candidates a decode-row list holds (clsa_prefill.hip)
+
 namespace {
 
 constexpr int kNT = 256;          // threads per workgroup
@@ -43,6 +53,12 @@ constexpr int kBuckets = 2048;    // histogram of the top 11 key bits
 constexpr int kBucketShift = 21;
 constexpr uint32_t kLowMask = (1u << kBucketShift) - 1u;
 constexpr int kMaxChunks = 4096;  // chunks per row
+constexpr int kMaxFilterCH = 1024;  // keys per chunk in filter mode (at most)
+
+// what route_score does with the scores
+constexpr int kHist = 0;    // top-k: keys + histogram of the top 11 bits
+constexpr int kCount = 1;   // threshold: keys + count of keys >= tau per chunk
+constexpr int kFilter = 2;  // top-k: candidates >= thr[r] into the chunk's segment
 
 struct RouteArgs {
   const void* q;          // [R][d]
@@ -64,6 +80,11 @@ struct RouteArgs {
   uint32_t* ccnt;         // [R][C]      candidates per chunk
   uint32_t* keys;         // [R][n_cap]
   uint64_t* cand;         // [R][n_cap]  chunk c's candidates at [c*CH, ...)
+  // filter mode
+  const uint16_t* samp;   // [R][kRowSamples] sampled key prefixes (row_sample)
+  uint32_t* rowcnt;       // [R]        candidates found (zeroed by the sampling kernel)
+  uint64_t* clist;        // [R][lcap]  position | score bits << 32, the first lcap kept
+  int lcap;
 };
 
 CLSA_DEV int64_t visible(const RouteArgs& a, int r) {
@@ -159,21 +180,72 @@ CLSA_DEV uint32_t block_sum_prefix(const uint32_t* arr, int64_t n, uint32_t* tmp
 }
 
 // ------------------------------------------------------------------- score
-template <typename T, int D, bool TOPK>
+template <typename T, int D, int MODE>
 __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
   constexpr int kEPL = Elem<T>::kPer16;        // elements per 16-byte segment
   constexpr int kLPR = D / kEPL;               // lanes per key row
   constexpr int kKPI = kWave / kLPR;           // key rows per wave load
   constexpr int kU = kLPR;                     // loads per lane per wave pass
   static_assert(kLPR >= 2 && kLPR <= 32, "unsupported row width");
+  constexpr bool TOPK = MODE == kHist;
 
   __shared__ uint32_t hist[TOPK ? kBuckets : 1];
   __shared__ uint32_t tmp[kNT / kWave];
+  __shared__ uint64_t cbuf[MODE == kFilter ? kMaxFilterCH : 1];  // the chunk's candidates
+  __shared__ uint32_t wh[MODE == kFilter ? 1024 : 1];
+  __shared__ uint32_t ccount;
+  __shared__ float sthr;
 
   const int c = blockIdx.x, r = blockIdx.y;
   const int tid = threadIdx.x, lane = lane_id(), w = tid / kWave;
   const int b = r / a.M;
   const int64_t n_vis = visible(a, r);
+  const int grp = lane / kLPR, pos = lane % kLPR;
+  float qf[kEPL];
+  Elem<T>::load_q(a.q, (size_t)r * D + (size_t)pos * kEPL, qf);
+  const char* Kb = static_cast<const char*>(a.K) + (size_t)b * a.n_cap * D * sizeof(T);
+  const int64_t j0 = (int64_t)c * a.CH;
+  u32x4_t v[kU];
+  // this wave's keys wbase .. wbase + 63 (rows past n_vis read row 0)
+  auto issue = [&](int64_t wbase) {
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t j = wbase + u * kKPI + grp;
+      const int64_t jj = j < n_vis ? j : 0;
+      v[u] = load_stream16(Kb + (size_t)jj * D * sizeof(T) + pos * 16);
+    }
+  };
+  bool pre = false;  // the wave's first keys are already in flight
+  float thr = 0.f;
+  if constexpr (MODE == kFilter) {
+    const int64_t k_eff = (int64_t)a.k < n_vis ? (int64_t)a.k : n_vis;
+    if (k_eff >= n_vis) return;  // every visible key is selected: no candidates needed
+    if (c >= chunks_of(n_vis, a.CH)) return;
+    // the row's threshold, ranked from its samples by wave 0 (-inf when
+    // the sample is too small to bound the k-th score), while every wave's
+    // first keys are already on their way
+    const RowPlan p = row_plan(n_vis, k_eff);
+    const bool ranks = p.rho <= p.ns;
+    const int64_t wb0 = j0 + w * kWave;
+    const uint16_t* srow = a.samp + (size_t)r * kRowSamples;
+    float t = -INFINITY;
+    // The compact list is read first (by every wave: 1 KB, no branch) and
+    // the keys after it, pinned in that order, so the ranking waits on the
+    // list alone.
+    uint32_t sv[kRowTop];
+    load_row_kept(srow, p, sv);
+    issue(wb0);
+    pre = true;
+    asm volatile("" ::: "memory");
+    if (w == 0 && ranks) t = p.compact ? rank_row_kept(sv, p, wh) : rank_row_samples(srow, p, wh);
+    if (w == 0 && lane == 0) {
+      sthr = t;
+      ccount = 0u;
+    }
+    // a barrier on LDS alone: the key loads stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    thr = sthr;
+  }
   if (c >= chunks_of(n_vis, a.CH)) return;
   if (TOPK) {
     if ((int64_t)a.k >= n_vis) return;  // every visible key is selected
@@ -181,33 +253,32 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
     __syncthreads();
   }
   uint32_t tkey = 0;
-  if (!TOPK) tkey = score_key(a.tau[r]);
+  if (MODE == kCount) tkey = score_key(a.tau[r]);
 
-  const int grp = lane / kLPR, pos = lane % kLPR;
-  float qf[kEPL];
-  Elem<T>::load_q(a.q, (size_t)r * D + (size_t)pos * kEPL, qf);
-
-  const char* Kb = static_cast<const char*>(a.K) + (size_t)b * a.n_cap * D * sizeof(T);
   uint32_t* keys_row = a.keys + (size_t)r * a.n_cap;
-  const int64_t j0 = (int64_t)c * a.CH;
   uint32_t n_ge = 0;
 
   for (int it = 0; it < a.CH / kNT; ++it) {
     const int64_t wbase = j0 + (int64_t)it * kNT + w * kWave;
     if (wbase >= n_vis) break;
     float part[kU];
-    u32x4_t v[kU];
-#pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      const int64_t j = wbase + u * kKPI + grp;
-      const int64_t jj = j < n_vis ? j : 0;
-      v[u] = load_stream16(Kb + (size_t)jj * D * sizeof(T) + pos * 16);
-    }
+    if (!(pre && it == 0)) issue(wbase);
 #pragma unroll
     for (int u = 0; u < kU; ++u) part[u] = Elem<T>::dot(v[u], qf);
     const float s = reduce_scatter<kU>(part, lane);
     const int64_t j = wbase + pos * kKPI + grp;
-    if (j < n_vis) {
+    if (MODE == kFilter) {
+      const bool hit = j < n_vis && s >= thr;
+      const uint64_t hm = __ballot(hit);
+      if (hm != 0ull) {  // wave-uniform
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&ccount, (uint32_t)__popcll(hm));
+        base = __builtin_amdgcn_readfirstlane(base);
+        if (hit)
+          cbuf[base + lanes_below(hm)] =
+              ((uint64_t)__float_as_uint(s) << 32) | (uint64_t)(uint32_t)j;
+      }
+    } else if (j < n_vis) {
       const uint32_t key = score_key(s);
       keys_row[j] = key;
       if (TOPK) atomicAdd(&hist[key >> kBucketShift], 1u);
@@ -215,7 +286,19 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
     }
   }
 
-  if (TOPK) {
+  if (MODE == kFilter) {
+    // the chunk's candidates, appended to the row's list (one reservation
+    // per workgroup; entries past the list's capacity are counted, not kept)
+    __syncthreads();
+    const uint32_t n = ccount;
+    if (n == 0u) return;
+    if (tid == 0) tmp[0] = atomicAdd(&a.rowcnt[r], n);
+    __syncthreads();
+    const uint32_t base = tmp[0];
+    uint64_t* dst = a.clist + (size_t)r * a.lcap;
+    for (uint32_t i = tid; i < n; i += kNT)
+      if (base + i < (uint32_t)a.lcap) dst[base + i] = cbuf[i];
+  } else if (TOPK) {
     __syncthreads();
     uint32_t* gh = a.ghist + (size_t)r * kBuckets;
     for (int i = tid; i < kBuckets; i += kNT) {
@@ -595,17 +678,39 @@ bool shape_ok(int B, int M, int d, int64_t n_cap, int cap) {
   return true;
 }
 
-template <bool TOPK>
+template <int MODE>
 void launch_score(const RouteArgs& a, clsa_dtype dt, int d, dim3 grid, hipStream_t s) {
   if (dt == CLSA_BF16) {
-    if (d == 32) hipLaunchKernelGGL((route_score<uint16_t, 32, TOPK>), grid, dim3(kNT), 0, s, a);
-    if (d == 64) hipLaunchKernelGGL((route_score<uint16_t, 64, TOPK>), grid, dim3(kNT), 0, s, a);
-    if (d == 128) hipLaunchKernelGGL((route_score<uint16_t, 128, TOPK>), grid, dim3(kNT), 0, s, a);
-  } else {
-    if (d == 32) hipLaunchKernelGGL((route_score<float, 32, TOPK>), grid, dim3(kNT), 0, s, a);
-    if (d == 64) hipLaunchKernelGGL((route_score<float, 64, TOPK>), grid, dim3(kNT), 0, s, a);
-    if (d == 128) hipLaunchKernelGGL((route_score<float, 128, TOPK>), grid, dim3(kNT), 0, s, a);
+    if (d == 32) hipLaunchKernelGGL((route_score<uint16_t, 32, MODE>), grid, dim3(kNT), 0, s, a);
+    if (d == 64) hipLaunchKernelGGL((route_score<uint16_t, 64, MODE>), grid, dim3(kNT), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((route_score<uint16_t, 128, MODE>), grid, dim3(kNT), 0, s, a);
+  } else if constexpr (MODE != kFilter) {
+    if (d == 32) hipLaunchKernelGGL((route_score<float, 32, MODE>), grid, dim3(kNT), 0, s, a);
+    if (d == 64) hipLaunchKernelGGL((route_score<float, 64, MODE>), grid, dim3(kNT), 0, s, a);
+    if (d == 128) hipLaunchKernelGGL((route_score<float, 128, MODE>), grid, dim3(kNT), 0, s, a);
   }
+}
+
+// Filter path workspace: keys per chunk chosen so that the score pass has
+// about a thousand workgroups (256 .. 1024 keys, a multiple of the block);
+// per row the samples, the candidate count and the candidate list.
+struct FilterLayout {
+  int CH, C;
+  size_t o_samp, o_cnt, o_cand, total;
+};
+
+FilterLayout filter_layout(int64_t R, int64_t n_cap) {
+  FilterLayout L{};
+  int64_t CH = kMaxFilterCH;
+  while (CH > kNT && R * ceil_div64(n_cap, CH) < 1024) CH /= 2;
+  L.CH = (int)CH;
+  L.C = (int)ceil_div64(n_cap, CH);
+  size_t o = 0;
+  L.o_samp = o; o = align_up(o + (size_t)R * kRowSamples * 2, 256);
+  L.o_cnt = o; o = align_up(o + (size_t)R * 4, 256);
+  L.o_cand = o; o = align_up(o + (size_t)R * seg_route_list_cap() * 8, 256);
+  L.total = o;
+  return L;
 }
 
 RouteArgs fill_args(const Layout& L, void* ws, const void* q_idx, const void* K_idx, int B, int M,
@@ -647,6 +752,14 @@ size_t block_route_workspace(int B, int M, int d, int64_t n_cap);
 int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
                 const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
                 int cap, void* ws, hipStream_t s);
+// Threshold and select of the filter path (clsa_prefill.hip).
+bool seg_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt);
+void seg_route_sample(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                      const int32_t* n_ctx, int64_t q_pos0, int k, uint16_t* samp,
+                      uint32_t* rowcnt, hipStream_t s);
+void seg_route_select(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                      const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
+                      int cap, uint32_t* rowcnt, uint64_t* cand, hipStream_t s);
 }  // namespace clsa
 
 using namespace clsa;
@@ -655,6 +768,7 @@ extern "C" size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, 
                                             clsa_dtype dt) {
   if (!shape_ok(B, M, d, n_cap, cap) || k < 1) return 0;
   if (block_route_applies(M, d, n_cap, k, dt)) return block_route_workspace(B, M, d, n_cap);
+  if (seg_route_applies(M, d, n_cap, k, dt)) return filter_layout((int64_t)B * M, n_cap).total;
   return make_layout((int64_t)B * M, n_cap, true).total;
 }
 
@@ -671,13 +785,40 @@ extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, in
     return block_route(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, ws, s);
   }
   const int64_t R = (int64_t)B * M;
+  if (seg_route_applies(M, d, n_cap, k, dt)) {
+    const FilterLayout F = filter_layout(R, n_cap);
+    if (!ws || ws_bytes < F.total) return CLSA_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    RouteArgs a{};
+    a.q = q_idx;
+    a.K = K_idx;
+    a.n_ctx = n_ctx;
+    a.n_cap = n_cap;
+    a.q_pos0 = q_pos0 < 0 ? -1 : q_pos0;
+    a.B = B;
+    a.M = M;
+    a.k = k;
+    a.cap = cap;
+    a.CH = F.CH;
+    a.C = F.C;
+    a.samp = reinterpret_cast<const uint16_t*>(base + F.o_samp);
+    a.rowcnt = reinterpret_cast<uint32_t*>(base + F.o_cnt);
+    a.clist = reinterpret_cast<uint64_t*>(base + F.o_cand);
+    a.lcap = seg_route_list_cap();
+    seg_route_sample(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k,
+                     reinterpret_cast<uint16_t*>(base + F.o_samp), a.rowcnt, s);
+    launch_score<kFilter>(a, dt, d, dim3((unsigned)F.C, (unsigned)R), s);
+    seg_route_select(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, a.rowcnt,
+                     a.clist, s);
+    return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
+  }
   const Layout L = make_layout(R, n_cap, true);
   if (!ws || ws_bytes < L.total) return CLSA_ERR_WORKSPACE;
   const RouteArgs a = fill_args(L, ws, q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, k, nullptr,
                                 idx, counts, cap);
   if (zero_fill(ws, L.ctrl_end, s) != hipSuccess) return CLSA_ERR_HIP;
   const dim3 grid((unsigned)L.C, (unsigned)R);
-  launch_score<true>(a, dt, d, grid, s);
+  launch_score<kHist>(a, dt, d, grid, s);
   hipLaunchKernelGGL(route_cands, grid, dim3(kNT), 0, s, a);
   hipLaunchKernelGGL(route_select, dim3((unsigned)R), dim3(kNT), 0, s, a);
   hipLaunchKernelGGL(route_compact<true>, grid, dim3(kNT), 0, s, a);
@@ -706,7 +847,7 @@ extern "C" int clsa_route_threshold(const void* q_idx, const void* K_idx, int B,
   const RouteArgs a = fill_args(L, ws, q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, 1, tau, idx,
                                 counts, cap);
   const dim3 grid((unsigned)L.C, (unsigned)R);
-  launch_score<false>(a, dt, d, grid, s);
+  launch_score<kCount>(a, dt, d, grid, s);
   hipLaunchKernelGGL(route_compact<false>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
 }

@@ -61,8 +61,13 @@ def test_route_workspace_sizes(lib):
     small = lib.clsa_route_workspace_size(1, 1, 64, 4096, 256, 256, BF16)
     big = lib.clsa_route_workspace_size(8, 1, 64, 131136, 2048, 2048, BF16)
     assert 0 < small < big
-    # keys (4 B) and candidates (8 B) per slot dominate
-    assert big >= 8 * 131136 * 12
+    # bf16 rows with k <= 2048: per row 4096 sampled 2-byte key prefixes, a
+    # count and a list of 6144 8-byte candidates, whatever the context length
+    assert big >= 8 * (4096 * 2 + 6144 * 8)
+    assert big == lib.clsa_route_workspace_size(8, 1, 64, 262144, 2048, 2048, BF16)
+    # otherwise (fp32, or k > 2048) keys (4 B) and candidates (8 B) per key
+    for dt, k in ((F32, 2048), (BF16, 4096)):
+        assert lib.clsa_route_workspace_size(8, 1, 64, 131136, k, k, dt) >= 8 * 131136 * 12
     assert lib.clsa_route_workspace_size(1, 1, 48, 4096, 256, 256, BF16) == 0  # bad d
     assert lib.clsa_route_threshold_workspace_size(16, 1, 128, 131072, 16384, BF16) > 0
     # a block of query rows on bf16 keys: sampled keys and candidate segments

@@ -120,6 +120,38 @@ def test_route_degenerate_bucket_uses_global_select(dtype):
     assert idx.cpu()[:, 0].tolist() == [list(range(7000))] * B
 
 
+@pytest.mark.parametrize("n", [3000, 20000])
+def test_route_bf16_zero_query_takes_lowest_positions(n):
+    # bf16 decode rows with k <= 2048 take the sampled-threshold path; every
+    # score is exactly 0, so every key passes the threshold (n = 3000 fits
+    # the select, n = 20000 overflows it and the row is rescanned)
+    K = torch.randn((2, n, 64), generator=_cpu_gen(15)).to(torch.bfloat16)
+    q = torch.zeros((2, 1, 64), dtype=torch.bfloat16)
+    for k in (100, 2048):
+        idx, counts = clsa.route(q.to(DEV), K.to(DEV), k, cap=k + 2)
+        gi = idx.cpu().numpy()
+        assert np.all(counts.cpu().numpy() == k)
+        assert np.all(gi[:, 0, :k] == np.arange(k)[None, :])
+        assert np.all(gi[:, 0, k:] == -1)
+
+
+def test_route_decode_sampled_outliers_force_rescan():
+    # the keys the threshold samples (positions floor(i n / 4096)) score far
+    # above the rest, so the sampled bound keeps fewer than k keys and each
+    # row is redone by the exact rescan
+    g = _cpu_gen(16)
+    B, n, d = 2, 40000, 64
+    at = torch.arange(4096, dtype=torch.int64) * n // 4096
+    u = torch.randn(d, generator=g)
+    u = u / u.norm()
+    K = 0.05 * torch.randn((B, n, d), generator=g)
+    K[:, at] = 3.0 * u + 0.2 * torch.randn((B, len(at), d), generator=g)
+    q = (u[None, None, :] + 0.1 * torch.randn((B, 1, d), generator=g)).to(torch.bfloat16)
+    K = K.to(torch.bfloat16)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 2048)
+    assert _check_route(idx, counts, q, K, [n, n], -1, 2048, 2048) <= 4
+
+
 def test_route_prefill_causal_rows():
     g = _cpu_gen(13)
     K = torch.randn((2, 3000, 64), generator=g).to(torch.bfloat16)
