@@ -464,9 +464,16 @@ Plan make_plan(int L, int B, int M, int Hq, int Hkv, int D, int cap, clsa_dtype 
   int64_t TS = (cap + S - 1) / S;
   TS = (TS + kTB - 1) / kTB * kTB;
   // Lists longer than a top-k budget (threshold selection) differ in length
-  // from row to row: splits of at most 512 spread the long ones over many
-  // workgroups (threshold lists at 128K: 721 -> 616 us per 16-layer call).
-  if (p.fast && cap > 2048 && TS > 512) TS = 512;
+  // from row to row: shorter splits spread the long ones over more
+  // workgroups (threshold lists of up to 8192 at 128K: 721 -> 616 us per
+  // 16-layer call with 512-key splits), but no more than 16 per row, so
+  // that very long uniform lists (dense attention) keep few, long splits.
+  if (p.fast && cap > 2048) {
+    int64_t lim = (cap + 15) / 16;
+    lim = (lim + kTB - 1) / kTB * kTB;
+    if (lim < 512) lim = 512;
+    if (TS > lim) TS = lim;
+  }
   p.TS = (int)TS;
   p.S = (int)((cap + TS - 1) / TS);
   size_t o = 0;
