@@ -302,8 +302,34 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
       const int i = lane + u * kWave;
       v[u] = i < ns ? row[i] : 0u;
     }
-    const uint32_t kth =
-        wave_kth_u16(v, [&](int u) { return lane + u * kWave < ns; }, (uint32_t)rho, h);
+    // Each lane keeps its 8 largest samples (an insertion chain: slot i
+    // becomes the median of slot i-1, slot i and the new value), and the
+    // wave ranks those 512: their rho-th largest is at most the rho-th
+    // largest sample (they are samples), and equal to it unless one lane
+    // held more than 8 of the top rho.  Ranking 512 keys instead of 4096
+    // keeps the histogram's LDS atomics off the critical path.  Samples
+    // past ns are 0, below every real key.
+    const int nv = ns > lane ? ((ns - lane + kWave - 1) / kWave < 8 ? (ns - lane + kWave - 1) / kWave : 8) : 0;
+    const bool compact = 2 * rho <= (int)wave_sum_u32((uint32_t)nv);
+    uint32_t kth;
+    if (compact) {
+      uint32_t t8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t8[i] = 0u;
+#pragma unroll
+      for (int u = 0; u < kThrNs / kWave; ++u) {
+        const uint32_t x = v[u];
+#pragma unroll
+        for (int i = 7; i >= 1; --i) {
+          const uint32_t lo = t8[i - 1] < x ? t8[i - 1] : x;
+          t8[i] = t8[i] > lo ? t8[i] : lo;
+        }
+        t8[0] = t8[0] > x ? t8[0] : x;
+      }
+      kth = wave_kth_u16(t8, [&](int u) { return u < nv; }, (uint32_t)rho, h);
+    } else {
+      kth = wave_kth_u16(v, [&](int u) { return lane + u * kWave < ns; }, (uint32_t)rho, h);
+    }
     // smallest float of the 16-bit bucket: never above the sample
     if (lane == 0) a.thr[r] = key_to_float(kth << 16);
   }

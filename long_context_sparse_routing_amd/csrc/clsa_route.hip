@@ -145,22 +145,44 @@ template <> struct Elem<uint16_t> {
   }
 };
 
+// The value of lane (lane ^ M): DPP moves within a 16-lane row for M <= 8
+// (quad permutes for 1 and 2, row shifts for 4 and 8), no LDS round trip.
+template <int M>
+CLSA_DEV float lane_xor(float v, int lane) {
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false));  // [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false));  // [2,3,0,1]
+  } else if constexpr (M == 4 || M == 8) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x110 + M, 0xf, 0xf, false);  // row_shr: lane - M
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x100 + M, 0xf, 0xf, false);  // row_shl: lane + M
+    return __int_as_float((lane & M) ? up : dn);
+  } else {
+    return __shfl_xor(v, M);
+  }
+}
+
 // U partial sums per lane, U consecutive lanes per key row.  After the
 // butterfly, the lane with in-group position p holds the full sum of partial
 // index p.  The addition tree is the same for every partial index, so
 // identical key rows give bit-identical scores.
+template <int U, int M = U / 2>
+CLSA_DEV void reduce_scatter_step(float (&v)[U], int lane) {
+  if constexpr (M >= 1) {
+    const bool up = (lane & M) != 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      const float send = up ? v[i] : v[i + M];
+      const float keep = up ? v[i + M] : v[i];
+      v[i] = keep + lane_xor<M>(send, lane);
+    }
+    reduce_scatter_step<U, M / 2>(v, lane);
+  }
+}
 template <int U>
 CLSA_DEV float reduce_scatter(float (&v)[U], int lane) {
-#pragma unroll
-  for (int m = U / 2; m >= 1; m >>= 1) {
-    const bool up = (lane & m) != 0;
-#pragma unroll
-    for (int i = 0; i < m; ++i) {
-      const float send = up ? v[i] : v[i + m];
-      const float keep = up ? v[i + m] : v[i];
-      v[i] = keep + __shfl_xor(send, m);
-    }
-  }
+  reduce_scatter_step<U>(v, lane);
   return v[0];
 }
 
