@@ -210,7 +210,7 @@ struct SelScratch {  // LDS scratch of the block selects
 // count with rho - 4 sqrt(rho) >= k * ns / n, so at least k keys of the row
 // score above the threshold with high probability; rows where it keeps
 // fewer (or too many) keys are caught by the select.
-constexpr int kThrRows = 16;  // rows per workgroup: one 16-row MFMA block
+constexpr int kThrRows = 16;  // rows per workgroup (<= 16, the MFMA block's rows; a multiple of 4)
 constexpr int kThrNs = 4096;  // sampled keys per row at most
 constexpr int kThrTiles = 8;  // 16-sample tiles whose loads are in flight together
 constexpr int kThrBins = 1024;
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
 #pragma unroll
     for (int st = 0; st < D / 32; ++st) {
       u32x4_t v = {0u, 0u, 0u, 0u};
-      if (m < a.M)
+      if (lane % 16 < kThrRows && m < a.M)
         v = *reinterpret_cast<const u32x4_t*>(a.q + ((size_t)b * a.M + m) * D + 32 * st +
                                                 8 * (lane / 16));
       qa[st] = __builtin_bit_cast(bf16x8_t, v);
@@ -271,7 +271,8 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
         const int64_t j = (int64_t)smp * a.ss;
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
-          sk[4 * (lane / 16) + jj][smp] = j < lim[jj] ? (uint16_t)(score_key(c[jj]) >> 16) : 0;
+          if (4 * (lane / 16) + jj < kThrRows)
+            sk[4 * (lane / 16) + jj][smp] = j < lim[jj] ? (uint16_t)(score_key(c[jj]) >> 16) : 0;
       }
     }
   }
@@ -825,10 +826,14 @@ CLSA_DEV uint32_t block_excl_scan_arr(const uint32_t* in, uint32_t* out, int n, 
 constexpr int kPerT = kSelCap / kNT;
 
 // Bitmap words each select thread owns (contiguous, a multiple of 4 so they
-// are read 16 bytes at a time); the bitmap covers kNT times that many words.
+// are read 16 bytes at a time); the bitmap covers kNT times that many words
+// and is followed by one prefix word per 4-word group.
 __host__ __device__ inline int select_words_per_thread(int64_t n_cap) {
   const int64_t w = ceil_div64(ceil_div64(n_cap, 32), kNT);
   return (int)((w + 3) / 4 * 4);
+}
+inline size_t select_lds_bytes(int64_t n_cap) {
+  return (size_t)select_words_per_thread(n_cap) * kNT * sizeof(uint32_t) * 5 / 4;
 }
 
 // CONTIG: the row's candidates are one contiguous list of segcnt[r] entries
@@ -836,7 +841,7 @@ __host__ __device__ inline int select_words_per_thread(int64_t n_cap) {
 // segments of a.kc entries each, segcnt[r][c] used.
 template <int D, bool CONTIG>
 __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
-  extern __shared__ u32x4_t bitmap4[];  // kNT * select_words_per_thread(n_cap) words
+  extern __shared__ u32x4_t bitmap4[];  // select_lds_bytes(n_cap): bitmap, then group prefixes
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(bitmap4);
   __shared__ uint32_t segoff[CONTIG ? 1 : kMaxSegs + 1];
   __shared__ SelScratch S;
@@ -858,7 +863,11 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   // offsets of the row's segments (one per key chunk)
   const int nseg = CONTIG ? 1 : a.nchunks;
   uint32_t n_c;
+  uint64_t pre[CONTIG ? kPerT : 1];  // contiguous list: every slot loaded with the count
   if constexpr (CONTIG) {
+    const uint64_t* row = a.seg + (size_t)r * kSelCap;
+#pragma unroll
+    for (int u = 0; u < kPerT; ++u) pre[u] = row[u * kNT + tid];
     n_c = a.segcnt[r];  // the true count, even past the list's capacity
   } else {
     n_c = block_excl_scan_arr(a.segcnt + (size_t)r * nseg, segoff, nseg, S.tmp, S.bc);
@@ -878,14 +887,10 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   const int cnt = (int)((n_c + kNT - 1 - (uint32_t)tid) / kNT);  // elements of this thread
   uint32_t key[kPerT], pos[kPerT];
   if constexpr (CONTIG) {
-    const uint64_t* row = a.seg + (size_t)r * kSelCap;
-    uint64_t e[kPerT];
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) e[u] = u < cnt ? row[u * kNT + tid] : 0ull;
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) {
-      key[u] = score_key(__uint_as_float((uint32_t)(e[u] >> 32)));
-      pos[u] = (uint32_t)e[u];
+      key[u] = score_key(__uint_as_float((uint32_t)(pre[u] >> 32)));
+      pos[u] = (uint32_t)pre[u];
     }
   } else {
     const uint32_t half = (uint32_t)a.kc;  // segment capacity
@@ -974,22 +979,34 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   }
   __syncthreads();
 
-  // emit in position order, the thread's words read 16 bytes at a time
+  // emit in position order: the output slot of a selected position is the
+  // number of marked positions below it -- a prefix over 4-word groups of
+  // the bitmap, then popcounts inside the group -- so every thread writes
+  // its own selected candidates independently
+  uint32_t* gpre = bitmap + (size_t)wpt * kNT;  // per 4-word group: marks before it
   uint32_t mine = 0;
   for (int i = w0; i < w0 + wpt; i += 4) {
     const u32x4_t x = bitmap4[i / 4];
     mine += __popc(x[0]) + __popc(x[1]) + __popc(x[2]) + __popc(x[3]);
   }
-  uint32_t slot = block_incl_scan<kNT>(mine, S.tmp) - mine;
+  uint32_t run = block_incl_scan<kNT>(mine, S.tmp) - mine;
   for (int i = w0; i < w0 + wpt; i += 4) {
     const u32x4_t x = bitmap4[i / 4];
+    gpre[i / 4] = run;
+    run += __popc(x[0]) + __popc(x[1]) + __popc(x[2]) + __popc(x[3]);
+  }
+  __syncthreads();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t word = x[e];
-      while (word != 0u) {
-        const int bit = __builtin_ctz(word);
-        out[slot++] = (int32_t)((uint32_t)(i + e) * 32u + (uint32_t)bit);
-        word &= word - 1u;
+  for (int u = 0; u < kPerT; ++u) {
+    if (u < cnt) {
+      const uint32_t p = pos[u];
+      const u32x4_t x = bitmap4[p >> 7];
+      const uint32_t e = (p >> 5) & 3u;
+      const uint32_t word = e == 0 ? x[0] : (e == 1 ? x[1] : (e == 2 ? x[2] : x[3]));
+      if ((word >> (p & 31u)) & 1u) {
+        uint32_t slot = gpre[p >> 7] + __popc(word & ((1u << (p & 31u)) - 1u));
+        slot += (e > 0 ? __popc(x[0]) : 0u) + (e > 1 ? __popc(x[1]) : 0u) + (e > 2 ? __popc(x[2]) : 0u);
+        out[slot] = (int32_t)p;
       }
     }
   }
@@ -1005,7 +1022,7 @@ void launch_block(const BlockArgs& a, hipStream_t s) {
                           (unsigned)a.B),
                      dim3(kFT), 0, s, a);
   hipLaunchKernelGGL((block_select<D, false>), dim3((unsigned)R), dim3(kNT),
-                     (size_t)select_words_per_thread(a.n_cap) * kNT * sizeof(uint32_t), s, a);
+                     select_lds_bytes(a.n_cap), s, a);
 }
 
 struct BlockLayout {
@@ -1125,7 +1142,7 @@ void seg_route_select(const void* q_idx, const void* K_idx, int B, int M, int d,
   a.segcnt = rowcnt;
   a.seg = cand;
   const dim3 grid((unsigned)(B * M));
-  const size_t lds = (size_t)select_words_per_thread(n_cap) * kNT * sizeof(uint32_t);
+  const size_t lds = select_lds_bytes(n_cap);
   if (d == 32) hipLaunchKernelGGL((block_select<32, true>), grid, dim3(kNT), lds, s, a);
   else if (d == 64) hipLaunchKernelGGL((block_select<64, true>), grid, dim3(kNT), lds, s, a);
   else hipLaunchKernelGGL((block_select<128, true>), grid, dim3(kNT), lds, s, a);
