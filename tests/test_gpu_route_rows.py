@@ -1,0 +1,99 @@
+"""GPU parity of routing for rows whose keys no other row shares (bf16,
+k <= 2048, up to 512K keys: a sampled per-row lower bound of the k-th
+score, one filtered scan, the exact select of the candidates) at the edges
+of that path, against the CPU oracle.
+
+Acceptance as in test_gpu_parity: equal counts, ascending lists with -1
+padding, index sets identical except at boundary pairs whose oracle scores
+lie within 1e-5 relative of the c-th largest score.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_routing_amd import binding as clsa
+from oracle import clsa_oracle as O
+from tests.parity_util import check_topk_row, f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _gen(seed):
+    g = torch.Generator()
+    g.manual_seed(seed)
+    return g
+
+
+def _check(idx, counts, q, K, n_ctx, q_pos0, k, cap, rows=None):
+    q_np, K_np = f64(q), f64(K)
+    B, M = q.shape[0], q.shape[1]
+    rows = rows if rows is not None else [(b, m) for b in range(B) for m in range(M)]
+    gi, gc = idx.cpu().numpy(), counts.cpu().numpy()
+    for b, m in rows:
+        nv = O.visible_count(n_ctx[b], q_pos0, m)
+        s = O.route_scores(q_np[b, m], K_np[b], nv)
+        sel = O.topk_select(s, k)
+        o_idx = np.full(cap, -1)
+        o_idx[: len(sel)] = sel
+        check_topk_row(gi[b, m], int(gc[b, m]), o_idx, len(sel), s, cap)
+
+
+@pytest.mark.parametrize("d", [32, 64, 128])
+@pytest.mark.parametrize("k", [300, 2048])
+def test_causal_query_rows_below_block_size(d, k):
+    # 16 causal query rows per sequence (a few tokens decoded at once):
+    # fewer than a matrix-core block, so every row is routed on its own
+    g = _gen(500 + d + k)
+    B, M, n = 2, 16, 20000
+    n_ctx = [n, n - 9]
+    K = torch.randn((B, n, d), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, M, d), generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), k, n_ctx=nc, q_pos0=n - M, cap=k + 4)
+    torch.cuda.synchronize()
+    _check(idx, counts, q, K, n_ctx, n - M, k, k + 4)
+
+
+@pytest.mark.parametrize("n", [2049, 2100, 4095, 4096, 4097, 8191, 8193])
+def test_context_lengths_around_the_sample_size(n):
+    # every key is a sample up to 4096 keys, then evenly spaced samples;
+    # just above k the bound keeps every key
+    g = _gen(600 + n)
+    K = torch.randn((3, n, 64), generator=g).to(torch.bfloat16)
+    q = (torch.randn((3, 1, 64), generator=g) / 8).to(torch.bfloat16)
+    n_ctx = [n, n - 1, n // 2 + 1]
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 2048, n_ctx=nc)
+    torch.cuda.synchronize()
+    _check(idx, counts, q, K, n_ctx, -1, 2048, 2048)
+
+
+@pytest.mark.parametrize("n_cap", [524288, 524289])
+def test_largest_context_of_the_path_and_past_it(n_cap):
+    # 512K keys is the largest context the sampled path takes; one more key
+    # goes to the exhaustive path.  Both must agree with the oracle.
+    g = _gen(700 + n_cap % 7)
+    K = torch.randn((1, n_cap, 64), generator=g).to(torch.bfloat16)
+    q = (torch.randn((1, 1, 64), generator=g) / 8).to(torch.bfloat16)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 2048)
+    torch.cuda.synchronize()
+    _check(idx, counts, q, K, [n_cap], -1, 2048, 2048)
+
+
+def test_many_sequences_one_launch():
+    # 40 sequences of different lengths in one call
+    g = _gen(800)
+    B, n = 40, 12000
+    n_ctx = [n - 250 * b for b in range(B)]
+    K = torch.randn((B, n, 64), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, 1, 64), generator=g) / 8).to(torch.bfloat16)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 1024, n_ctx=nc)
+    torch.cuda.synchronize()
+    _check(idx, counts, q, K, n_ctx, -1, 1024, 1024, rows=[(b, 0) for b in range(0, B, 3)])
