@@ -31,7 +31,7 @@
 namespace clsa {
 namespace {
 
-constexpr int kNT = 256;           // threads of the thresh/select kernels
+constexpr int kNT = 512;           // threads of the thresh/select kernels
 constexpr int kFT = 512;           // threads of the filter kernel (8 waves)
 constexpr int kSStride = 32;       // sampling stride of the threshold estimate
 constexpr int kStageKeys = 64;     // keys per filter step (two 32-key tiles)
