@@ -275,6 +275,15 @@ def test_attn_bf16_fast_shapes(Hq, Hkv, D):
     _check_attn(*case)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 8, 64), (64, 4, 64), (16, 2, 256)])
+def test_attn_bf16_rows_sharing_positions(Hq, Hkv, D):
+    # 48 query rows of one sequence pick 160 of 1500 positions each, so every
+    # K/V row is read about five times per layer: the launch keeps gathered
+    # rows in the caches instead of streaming them
+    case = _attn_case(torch.bfloat16, 2, 1, 48, Hq, Hkv, D, 1500, 160, [160, 97, 1, 0], 31 + D)
+    _check_attn(*case)
+
+
 def test_attn_bf16_generic_head_dim():
     case = _attn_case(torch.bfloat16, 2, 2, 2, 8, 2, 96, 3000, 300, [300, 17, 0, 64], 23)
     _check_attn(*case)
