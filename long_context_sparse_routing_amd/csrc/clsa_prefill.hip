@@ -40,17 +40,19 @@ constexpr int kMaxK = 2048;
 constexpr int kMaxSegs = 2048;     // candidate segments (key chunks) per row
 constexpr int64_t kMaxKeys = 524288;
 
-// Keys held in LDS by a filter workgroup at a time (64 KB of bf16 keys),
+// Keys held in LDS by a filter workgroup at a time (16 KB of bf16 keys),
 // and keys per candidate segment: a workgroup walks kSubPerChunk of those
-// in turn, so a row's segment of one chunk covers 4x as many keys and its
+// in turn, so a row's segment of one chunk covers 16x as many keys and its
 // cache lines fill before they are written back.
-constexpr int sub_keys(int d) { return 32768 / d; }
-constexpr int kSubPerChunk = 4;
+constexpr int sub_keys(int d) { return 8192 / d; }
+constexpr int kSubPerChunk = 16;
 constexpr int chunk_keys(int d) { return kSubPerChunk * sub_keys(d); }
-// Filter rows per workgroup (one slab pair per wave): with 32 workgroups
-// per XCD this keeps the partly filled segment lines in flight (one per
-// row) within the XCD's 4 MB L2, so they fill before they are written back.
-constexpr int kMaxRowsPerGroup = 512;
+// Filter rows per workgroup (one 32-row slab per wave).  16 KB of keys and
+// 64 KB of hit scratch let two workgroups share a CU, four waves per SIMD,
+// so one wave's hit extraction overlaps another's matrix work; the 64
+// workgroups of an XCD keep their partly filled segment lines (one per row)
+// within its 4 MB L2, so they fill before they are written back.
+constexpr int kMaxRowsPerGroup = 256;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
@@ -415,10 +417,10 @@ __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
 }
 
 // ------------------------------------------------------------------ filter
-// Each workgroup holds one chunk of chunk_keys(d) keys in LDS for its whole
-// life and its 8 waves stream 64-row query slab pairs through registers:
-// no barrier inside the loop, and the chunk is read from HBM once per
-// workgroup.
+// Each workgroup walks one chunk of chunk_keys(d) keys, sub_keys(d) at a
+// time in LDS, and each of its 8 waves keeps one 32-row query slab in
+// registers for the whole chunk: no barrier inside a sub-chunk, and the
+// chunk is read from HBM once per workgroup.
 //
 // A last MFMA k-step against a constant column subtracts the row's
 // threshold inside the accumulator: dd = score - T', with T' the threshold
@@ -426,10 +428,13 @@ __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
 // bits of a step's 32 values per lane pack into one hit mask with one
 // v_alignbit each; lanes with hits spill their 32 values to LDS scratch and
 // up to four hits per lane per pass are appended as (dd, position) to the
-// row's segment in HBM, the two lanes of a row one after the other.  Rows that keep every key (threshold -inf) and
-// tiles crossing a row's visibility limit take explicit compares instead.
-constexpr int kScrStride = 36;  // scratch words per lane (32 values, padded
-                                // so 16 consecutive lanes hit distinct banks)
+// row's segment in HBM, the two lanes of a row one after the other.  Rows
+// that keep every key (threshold -inf) and tiles crossing a row's
+// visibility limit take explicit compares instead.
+constexpr int kScrStride = 32;  // scratch words per lane: the step's 32 values
+// 16-byte piece q of a lane's scratch sits in slot q ^ (lane & 7), so the 8
+// lanes a 128-bit LDS access serves at once hit distinct banks.
+CLSA_DEV int scr_slot(int q, int lane) { return q ^ (lane & 7); }
 
 // bf16 bits of -x, with x first rounded down to bf16 (toward -inf)
 CLSA_DEV uint16_t neg_bf16_floor(float x) {
@@ -474,20 +479,26 @@ CLSA_DEV uint32_t stage_hits(const f32x16_t& x0, const f32x16_t& x1, const SlabS
   return ~m;
 }
 
-// Spill the step's values of lanes with hits to scratch, then append the
-// hits (dd, position) to the row's segment, up to four per lane per pass
-// so that each pass waits on LDS once.
+// Spill the step's values of lanes with hits to scratch (each 32-key tile
+// only where it holds a hit), then append the hits (dd, position) to the
+// row's segment, up to four per lane per pass so that each pass waits on
+// LDS once.  Value i of a lane is key jl0 + i + (i & 28).
 CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, SlabState& st,
                          int32_t jl0, float* scr) {
-  if (hits != 0u) {
+  const int lane = lane_id();
+  if ((hits & 0xffffu) != 0u) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      reinterpret_cast<float4*>(scr)[q] =
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<float4*>(scr)[scr_slot(q, lane)] =
           make_float4(x0[4 * q], x0[4 * q + 1], x0[4 * q + 2], x0[4 * q + 3]);
-      reinterpret_cast<float4*>(scr)[4 + q] =
-          make_float4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3]);
-    }
   }
+  if ((hits >> 16) != 0u) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<float4*>(scr)[scr_slot(4 + q, lane)] =
+          make_float4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3]);
+  }
+  const int sw = (lane & 7) << 2;  // word i of the lane's values sits at i ^ sw
   while (__ballot(hits != 0u) != 0) {
     int idx[4];
     float dv[4];
@@ -498,15 +509,15 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
       h &= h - 1u;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q]];
+    for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q] ^ sw];
     const uint32_t n = __popc(hits) - __popc(h);  // hits taken this pass (<= 4)
     // lanes l and l+32 hold the same row: one stream, the upper lane after
     // the lower one
     const uint32_t n_pair = __shfl_xor(n, 32);
-    const uint32_t at = st.gcnt + (lane_id() >= 32 ? n_pair : 0u);
+    const uint32_t at = st.gcnt + (lane >= 32 ? n_pair : 0u);
     uint32_t pw[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)((jl0 + 2 * (idx[q] & 28)) | (idx[q] & 3));
+    for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)(jl0 + idx[q] + (idx[q] & 28));
     // exactly the pass's n entries (the partner lane's follow them): pairs
     // as 16-byte stores, an odd last one as 8 bytes
     uint64_t* dst = st.segp + at;
@@ -525,140 +536,109 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
   }
 }
 
-// Query operands and per-row state of the slab pair at rows p0 .. p0+63
+// Query operands and per-row state of the slab at rows m0 .. m0+31
 template <int D>
-CLSA_DEV void load_pair(const BlockArgs& a, int b, int p0, int ch, bf16x8_t (&qb)[2][D / 16],
-                        SlabState (&st)[2]) {
+CLSA_DEV void load_slab(const BlockArgs& a, int b, int m0, int ch, bf16x8_t (&qb)[D / 16],
+                        SlabState& st) {
   const int lane = lane_id();
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int m0 = p0 + blk * 32;
-    const int m = m0 + lane % 32;
-    const bool ok = m < a.M;
-    load_q_slab<D>(a, b, m0, qb[blk]);
-    const float T = ok ? a.thr[(size_t)b * a.M + m] : INFINITY;
-    const bool all = T == -INFINITY;
-    st[blk].tq = __builtin_bit_cast(
-        bf16x8_t, u32x4_t{lane < 32 ? (uint32_t)(all ? 0u : neg_bf16_floor(T)) : 0u, 0u, 0u, 0u});
-    st[blk].lo = all ? -INFINITY : 0.f;
-    st[blk].lim = ok ? (int32_t)row_visible(a, b, m) : 0;
-    st[blk].lim_min = (m0 + 31 < a.M) ? (int32_t)row_visible(a, b, m0) : 0;
-    st[blk].sign_ok = __ballot(all) == 0;
-    const size_t sg = ((size_t)b * a.M + (ok ? m : 0)) * a.nchunks + ch;
-    st[blk].segp = a.seg + sg * (size_t)a.kc;
-    st[blk].gcnt = 0;
-  }
+  const int m = m0 + lane % 32;
+  const bool ok = m < a.M;
+  load_q_slab<D>(a, b, m0, qb);
+  const float T = ok ? a.thr[(size_t)b * a.M + m] : INFINITY;
+  const bool all = T == -INFINITY;
+  st.tq = __builtin_bit_cast(
+      bf16x8_t, u32x4_t{lane < 32 ? (uint32_t)(all ? 0u : neg_bf16_floor(T)) : 0u, 0u, 0u, 0u});
+  st.lo = all ? -INFINITY : 0.f;
+  st.lim = ok ? (int32_t)row_visible(a, b, m) : 0;
+  st.lim_min = (m0 + 31 < a.M) ? (int32_t)row_visible(a, b, m0) : 0;
+  st.sign_ok = __ballot(all) == 0;
+  const size_t sg = ((size_t)b * a.M + (ok ? m : 0)) * a.nchunks + ch;
+  st.segp = a.seg + sg * (size_t)a.kc;
+  st.gcnt = 0;
 }
 
 // grid: (nchunks, ceil(M / rows_pg), B); rows_pg <= kMaxRowsPerGroup, a
-// multiple of 64.  Wave w owns slab pairs w, w + 8, ... of the group (two at
-// most) and keeps their segment counts across the sub-chunks.
+// multiple of 32.  Wave w owns the slab at rows r_lo + 32 w and keeps its
+// operands and segment counts across the sub-chunks.
 template <int D>
-__global__ __launch_bounds__(kFT) void block_filter(BlockArgs a) {
+__global__ __launch_bounds__(kFT) __attribute__((amdgpu_waves_per_eu(D <= 64 ? 4 : 2, 8)))
+void block_filter(BlockArgs a) {
   constexpr int KS = sub_keys(D);
   constexpr int P = D / 8;  // 16-byte pieces per key
-  constexpr int kPairs = kMaxRowsPerGroup / 64 / (kFT / kWave);
   __shared__ u32x4_t kc[KS * P];
   __shared__ __attribute__((aligned(16))) float scratch[kFT / kWave][kWave * kScrStride];
   const int ch = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int r_lo = g * a.rows_pg;
   const int r_hi = r_lo + a.rows_pg < a.M ? r_lo + a.rows_pg : a.M;
   const int64_t vis_hi = row_visible(a, b, r_hi - 1);  // visibility grows with m
   float* scr = &scratch[w][lane * kScrStride];
   const bf16x8_t kone =  // constant operand of the threshold k-step: 1.0 in dim 0
       __builtin_bit_cast(bf16x8_t, u32x4_t{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
-  uint32_t gcnt[kPairs][2];
-#pragma unroll
-  for (int pp = 0; pp < kPairs; ++pp) gcnt[pp][0] = gcnt[pp][1] = 0u;
+  const int m0 = r_lo + 32 * w;
+  const bool active = m0 < r_hi;  // wave-uniform
+  bf16x8_t qb[D / 16];
+  SlabState st;
+  int64_t vis_slab = 0;  // keys visible to the slab's last row
+  if (active) {
+    load_slab<D>(a, b, m0, ch, qb, st);
+    vis_slab = row_visible(a, b, (m0 + 31 < r_hi ? m0 + 31 : r_hi - 1));
+  }
 
   for (int sc = 0; sc < kSubPerChunk; ++sc) {
     const int64_t key_lo = (int64_t)ch * a.kc + (int64_t)sc * KS;
     const int64_t key_hi = key_lo + KS < vis_hi ? key_lo + KS : vis_hi;
     if (key_lo >= key_hi) break;  // uniform: nothing further is visible
     if (sc > 0) __syncthreads();  // the previous sub-chunk is no longer read
-    // the sub-chunk's keys, zeros at or beyond key_hi; loads issued in groups
+    // the sub-chunk's keys, zeros at or beyond key_hi
     {
       constexpr int kPer = KS * P / kFT;
+      u32x4_t v[kPer];
 #pragma unroll
-      for (int u0 = 0; u0 < kPer; u0 += 8) {
-        u32x4_t v[8];
+      for (int u = 0; u < kPer; ++u) {
+        const int i = threadIdx.x + u * kFT;
+        const int64_t j = key_lo + i / P;
+        v[u] = u32x4_t{0u, 0u, 0u, 0u};
+        if (j < key_hi)
+          v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % P) * 8);
+      }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = threadIdx.x + (u0 + u) * kFT;
-          const int64_t j = key_lo + i / P;
-          v[u] = u32x4_t{0u, 0u, 0u, 0u};
-          if (u0 + u < kPer && j < key_hi)
-            v[u] = *reinterpret_cast<const u32x4_t*>(a.K + ((size_t)b * a.n_cap + j) * D + (i % P) * 8);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int i = threadIdx.x + (u0 + u) * kFT;
-          if (u0 + u < kPer) kc[lds_piece<D>(i / P, i % P)] = v[u];
-        }
+      for (int u = 0; u < kPer; ++u) {
+        const int i = threadIdx.x + u * kFT;
+        kc[lds_piece<D>(i / P, i % P)] = v[u];
       }
     }
     __syncthreads();
+    if (!active) continue;
 
-#pragma unroll
-    for (int pp = 0; pp < kPairs; ++pp) {
-      const int p0 = r_lo + (w + pp * (kFT / kWave)) * 64;
-      if (p0 >= r_hi) break;
-      bf16x8_t qb[2][D / 16];
-      SlabState st[2];
-      load_pair<D>(a, b, p0, ch, qb, st);
-      st[0].gcnt = gcnt[pp][0];
-      st[1].gcnt = gcnt[pp][1];
-      const int nslab = (r_hi - p0 + 31) / 32 < 2 ? 1 : 2;
-      const int p_last = p0 + 63 < r_hi - 1 ? p0 + 63 : r_hi - 1;
-      const int64_t vis_p = row_visible(a, b, p_last);
-      const int64_t hi_p = key_hi < vis_p ? key_hi : vis_p;
-      const int nstage = hi_p > key_lo ? (int)((hi_p - key_lo + kStageKeys - 1) / kStageKeys) : 0;
-      for (int sidx = 0; sidx < nstage; ++sidx) {
-        const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // step start
-        const int32_t jl0 = js + 4 * (lane / 32);
-        bf16x8_t kb0[D / 16], kb1[D / 16];
-        load_k_tile<D>(kc, 2 * sidx, kb0);
-        load_k_tile<D>(kc, 2 * sidx + 1, kb1);
-        // rows: keys, columns: queries; the last k-step subtracts T'
-        f32x16_t x[2][2];
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          if (blk < nslab) {
-            x[blk][0] = tile_mma<D>(kb0, qb[blk], f32x16_t{});
-            x[blk][1] = tile_mma<D>(kb1, qb[blk], f32x16_t{});
-            x[blk][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][0], 0, 0, 0);
-            x[blk][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st[blk].tq, x[blk][1], 0, 0, 0);
-          }
-        }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          if (blk >= nslab) break;
-          SlabState& S = st[blk];
-          // wave-uniform: a scalar branch keeps the compare path out of the
-          // fast one
-          const bool fast = __builtin_amdgcn_readfirstlane(
-                                (int)(S.sign_ok && js + kStageKeys <= S.lim_min)) != 0;
-          uint32_t hits;
-          if (fast) hits = stage_hits<false>(x[blk][0], x[blk][1], S, jl0);
-          else hits = stage_hits<true>(x[blk][0], x[blk][1], S, jl0);
-          stage_emit(x[blk][0], x[blk][1], hits, S, jl0, scr);
-        }
-      }
-      gcnt[pp][0] = st[0].gcnt;
-      gcnt[pp][1] = st[1].gcnt;
+    const int64_t hi_p = key_hi < vis_slab ? key_hi : vis_slab;
+    const int nstage = hi_p > key_lo ? (int)((hi_p - key_lo + kStageKeys - 1) / kStageKeys) : 0;
+    for (int sidx = 0; sidx < nstage; ++sidx) {
+      const int32_t js = (int32_t)(key_lo + (int64_t)sidx * kStageKeys);  // step start
+      const int32_t jl0 = js + 4 * (lane / 32);
+      bf16x8_t kb0[D / 16], kb1[D / 16];
+      load_k_tile<D>(kc, 2 * sidx, kb0);
+      load_k_tile<D>(kc, 2 * sidx + 1, kb1);
+      // rows: keys, columns: queries; the last k-step subtracts T'
+      f32x16_t x0 = tile_mma<D>(kb0, qb, f32x16_t{});
+      f32x16_t x1 = tile_mma<D>(kb1, qb, f32x16_t{});
+      x0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st.tq, x0, 0, 0, 0);
+      x1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, st.tq, x1, 0, 0, 0);
+      // wave-uniform: a scalar branch keeps the compare path out of the
+      // fast one
+      const bool fast = __builtin_amdgcn_readfirstlane(
+                            (int)(st.sign_ok && js + kStageKeys <= st.lim_min)) != 0;
+      uint32_t hits;
+      if (fast) hits = stage_hits<false>(x0, x1, st, jl0);
+      else hits = stage_hits<true>(x0, x1, st, jl0);
+      stage_emit(x0, x1, hits, st, jl0, scr);
     }
   }
   // every (row, chunk) of the group gets its count, zero when it saw nothing
-#pragma unroll
-  for (int pp = 0; pp < kPairs; ++pp) {
-    const int p0 = r_lo + (w + pp * (kFT / kWave)) * 64;
-    if (p0 >= r_hi) break;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int m = p0 + blk * 32 + lane % 32;
-      if (m < r_hi && lane < 32) a.segcnt[((size_t)b * a.M + m) * a.nchunks + ch] = gcnt[pp][blk];
-    }
+  if (active) {
+    const int m = m0 + lane % 32;
+    if (m < r_hi && lane < 32) a.segcnt[((size_t)b * a.M + m) * a.nchunks + ch] = st.gcnt;
   }
 }
 
@@ -1080,10 +1060,10 @@ int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64
   a.kc = L.kc;
   a.nchunks = L.nchunks;
   // rows per filter workgroup: enough workgroups to cover the chip once,
-  // in multiples of a slab pair
+  // in multiples of a 32-row slab
   const int64_t want_groups = ceil_div64(256, (int64_t)L.nchunks * B);
   int64_t rows_pg = ceil_div64(M, want_groups < 1 ? 1 : want_groups);
-  rows_pg = (rows_pg + 63) / 64 * 64;
+  rows_pg = (rows_pg + 31) / 32 * 32;
   a.rows_pg = (int)(rows_pg < kMaxRowsPerGroup ? rows_pg : kMaxRowsPerGroup);
   a.thr = reinterpret_cast<float*>(base + L.o_thr);
   a.segcnt = reinterpret_cast<uint32_t*>(base + L.o_cnt);
