@@ -512,9 +512,11 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
     for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q] ^ sw];
     const uint32_t n = __popc(hits) - __popc(h);  // hits taken this pass (<= 4)
     // lanes l and l+32 hold the same row: one stream, the upper lane after
-    // the lower one
-    const uint32_t n_pair = __shfl_xor(n, 32);
-    const uint32_t at = st.gcnt + (lane >= 32 ? n_pair : 0u);
+    // the lower one.  Swapping the wave's halves gives every lane the lower
+    // lane's count (sw2[0] in the upper half) and the pair's total.
+    const auto sw2 = __builtin_amdgcn_permlane32_swap(n, n, false, false);
+    const uint32_t pair_total = sw2[0] + sw2[1];
+    const uint32_t at = st.gcnt + (lane >= 32 ? sw2[0] : 0u);
     uint32_t pw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)(jl0 + idx[q] + (idx[q] & 28));
@@ -531,7 +533,7 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
           u32x4_t{pw[2], __float_as_uint(dv[2]), pw[3], __float_as_uint(dv[3])};
     else if (n == 3u)
       dst[2] = ((uint64_t)__float_as_uint(dv[2]) << 32) | pw[2];
-    st.gcnt += n + n_pair;
+    st.gcnt += pair_total;
     hits = h;
   }
 }
