@@ -203,27 +203,35 @@ struct SelScratch {  // LDS scratch of the block selects
 
 // ------------------------------------------------------------------ thresh
 // One workgroup per 16 query rows.  Scores against every a.ss-th key come
-// from v_mfma_f32_16x16x32_bf16 and stay in LDS as the top 16 bits of their
-// order-preserving keys.  Each wave then takes its rows one at a time: the
-// samples go to registers, a 1024-bin histogram spans their actual key range
-// and a second pass resolves the boundary bin, which gives the rho-th
-// largest 16-bit key; the threshold is the smallest float with that key
-// prefix -- never above the sample.  rho is the smallest
+// from v_mfma_f32_16x16x32_bf16; as they come out of the accumulator, each
+// lane keeps, per row, the 8 largest top-16-bit prefixes of their
+// order-preserving keys among the samples it sees (an insertion chain: slot
+// i becomes the median of slot i-1, slot i and the new value).  The 128
+// such lists of a row (8 waves x 16 sample lanes, 1024 prefixes) go to LDS,
+// and a wave ranks each of its rows' lists: a 1024-bin histogram over their
+// actual range and a second pass over the boundary bin give the rho-th
+// largest.  The lists are samples, so that prefix is at most the rho-th
+// largest sample's, and equal to it unless one list held more than 8 of the
+// top rho (rho <= 105 for k <= 2048 here); the threshold is the smallest
+// float with that prefix -- never above the sample.  rho is the smallest
 // count with rho - 4 sqrt(rho) >= k * ns / n, so at least k keys of the row
 // score above the threshold with high probability; rows where it keeps
 // fewer (or too many) keys are caught by the select.
 constexpr int kThrRows = 16;  // rows per workgroup (<= 16, the MFMA block's rows; a multiple of 4)
 constexpr int kThrNs = 4096;  // sampled keys per row at most
-constexpr int kThrTiles = 8;  // 16-sample tiles whose loads are in flight together
+constexpr int kThrTiles = 4;  // 16-sample tiles whose loads are in flight together
 constexpr int kThrBins = 1024;
+constexpr int kThrTop = 8;    // prefixes each lane keeps per row
+constexpr int kThrKept = kNT / kWave * 16 * kThrTop;  // kept prefixes per row
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 template <int D>
 __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
-  __shared__ uint16_t sk[kThrRows][kThrNs];
+  __shared__ uint16_t kept[kThrRows][kThrKept];
   __shared__ uint32_t wh[kNT / kWave][kThrBins];
   const int m0 = blockIdx.x * kThrRows, b = blockIdx.y;
-  const int lane = lane_id(), w = threadIdx.x / kWave;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 
   // A operand: row m0 + lane%16, dims 32*st + 8*(lane/16) .. +7
   bf16x8_t qa[D / 32];
@@ -245,6 +253,11 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
     const int m = m0 + 4 * (lane / 16) + j;
     lim[j] = m < a.M ? row_visible(a, b, m) : 0;
   }
+  uint32_t t8[4][kThrTop];  // per row: this lane's largest prefixes, descending; 0 = none
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < kThrTop; ++i) t8[j][i] = 0u;
   const int ntile = (a.ns_max + 15) / 16;
   for (int t0 = w * kThrTiles; t0 < ntile; t0 += (kNT / kWave) * kThrTiles) {
     bf16x8_t kb[kThrTiles][D / 32];
@@ -263,19 +276,32 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < kThrTiles; ++u) {
-      if (t0 + u >= ntile) break;
       f32x4_t c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int st = 0; st < D / 32; ++st)
         c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], kb[u][st], c, 0, 0, 0);
-      const int smp = (t0 + u) * 16 + lane % 16;
-      if (smp < a.ns_max) {
-        const int64_t j = (int64_t)smp * a.ss;
+      const int64_t smp = (int64_t)(t0 + u) * 16 + lane % 16;
+      const int64_t j = smp * a.ss;
+      const bool in = t0 + u < ntile && smp < a.ns_max;
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-          if (4 * (lane / 16) + jj < kThrRows)
-            sk[4 * (lane / 16) + jj][smp] = j < lim[jj] ? (uint16_t)(score_key(c[jj]) >> 16) : 0;
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t x = (in && j < lim[jj]) ? score_key(c[jj]) >> 16 : 0u;
+#pragma unroll
+        for (int i = kThrTop - 1; i >= 1; --i) {
+          const uint32_t lo = t8[jj][i - 1] < x ? t8[jj][i - 1] : x;
+          t8[jj][i] = t8[jj][i] > lo ? t8[jj][i] : lo;
+        }
+        t8[jj][0] = t8[jj][0] > x ? t8[jj][0] : x;
       }
+    }
+  }
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int rl = 4 * (lane / 16) + jj;
+    if (rl < kThrRows) {
+      uint16_t* dst = &kept[rl][(w * 16 + lane % 16) * kThrTop];
+#pragma unroll
+      for (int i = 0; i < kThrTop; ++i) dst[i] = (uint16_t)t8[jj][i];
     }
   }
   __syncthreads();
@@ -293,46 +319,22 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
     }
     const int ns = (int)((n_vis + a.ss - 1) / a.ss);  // visible samples
     const int rho = sample_rank(n_vis, k_eff, ns);
-    if (rho > ns) {  // too few samples to bound the k-th score: keep every key
+    // the row's kept prefixes (lane l: entries l, l+64, ...); 0 marks an
+    // empty slot (no real key has a zero prefix)
+    uint32_t v[kThrKept / kWave];
+    uint32_t nk = 0;
+#pragma unroll
+    for (int u = 0; u < kThrKept / kWave; ++u) {
+      v[u] = kept[rl][lane + u * kWave];
+      nk += v[u] != 0u ? 1u : 0u;
+    }
+    if (rho > ns || (uint32_t)rho > wave_sum_u32(nk)) {
+      // too few samples to bound the k-th score: keep every key
       if (lane == 0) a.thr[r] = -INFINITY;
       continue;
     }
-    // the row's samples in registers (lane l: samples l, l+64, ...)
-    const uint16_t* row = sk[rl];
-    uint32_t v[kThrNs / kWave];
-#pragma unroll
-    for (int u = 0; u < kThrNs / kWave; ++u) {
-      const int i = lane + u * kWave;
-      v[u] = i < ns ? row[i] : 0u;
-    }
-    // Each lane keeps its 8 largest samples (an insertion chain: slot i
-    // becomes the median of slot i-1, slot i and the new value), and the
-    // wave ranks those 512: their rho-th largest is at most the rho-th
-    // largest sample (they are samples), and equal to it unless one lane
-    // held more than 8 of the top rho.  Ranking 512 keys instead of 4096
-    // keeps the histogram's LDS atomics off the critical path.  Samples
-    // past ns are 0, below every real key.
-    const int nv = ns > lane ? ((ns - lane + kWave - 1) / kWave < 8 ? (ns - lane + kWave - 1) / kWave : 8) : 0;
-    const bool compact = 2 * rho <= (int)wave_sum_u32((uint32_t)nv);
-    uint32_t kth;
-    if (compact) {
-      uint32_t t8[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t8[i] = 0u;
-#pragma unroll
-      for (int u = 0; u < kThrNs / kWave; ++u) {
-        const uint32_t x = v[u];
-#pragma unroll
-        for (int i = 7; i >= 1; --i) {
-          const uint32_t lo = t8[i - 1] < x ? t8[i - 1] : x;
-          t8[i] = t8[i] > lo ? t8[i] : lo;
-        }
-        t8[0] = t8[0] > x ? t8[0] : x;
-      }
-      kth = wave_kth_u16(t8, [&](int u) { return u < nv; }, (uint32_t)rho, h);
-    } else {
-      kth = wave_kth_u16(v, [&](int u) { return lane + u * kWave < ns; }, (uint32_t)rho, h);
-    }
+    const uint32_t kth =
+        wave_kth_u16(v, [&](int u) { return v[u] != 0u; }, (uint32_t)rho, h);
     // smallest float of the 16-bit bucket: never above the sample
     if (lane == 0) a.thr[r] = key_to_float(kth << 16);
   }
