@@ -9,17 +9,18 @@
 // matrix never reaches HBM.
 //
 //   block_thresh   per group of 16 rows: scores against every ss-th key
-//                  (MFMA), kept in LDS as 16-bit key prefixes; per row a
-//                  lower bound of the rho-th largest sampled score, rho
-//                  chosen so that, with a four-sigma margin, at least k keys
-//                  of the row score that much.  It becomes the row's filter
-//                  threshold T.
+//                  (MFMA), each lane keeping per row the largest 16-bit key
+//                  prefixes it sees; per row a lower bound of the rho-th
+//                  largest sampled score, rho chosen so that, with a
+//                  four-sigma margin, at least k keys of the row score that
+//                  much.  It becomes the row's filter threshold T.
 //   block_filter   the full score matrix in 32x32 MFMA tiles, keys as the A
 //                  operand and queries as B, so each lane owns one query
 //                  column (two lanes per row, one per key half); a workgroup
-//                  keeps key chunks in LDS and streams query rows through
-//                  them.  Keys scoring >= T are appended as (score - T',
-//                  position) to the row's segment of the chunk.
+//                  streams a key chunk through LDS while each wave keeps one
+//                  32-row query slab in registers.  Keys scoring >= T are
+//                  appended as (score - T', position) to the row's segment
+//                  of the chunk.
 //   block_select   per row: the exact top-k among the candidates (lower
 //                  positions win ties), written in ascending order.  A row
 //                  whose threshold kept fewer than k keys, or more than the
