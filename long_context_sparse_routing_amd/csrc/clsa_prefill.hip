@@ -710,6 +710,10 @@ template <int NPER>
 CLSA_DEV uint32_t kth_regs(const uint32_t (&k)[NPER], int cnt, uint32_t rank, SelScratch& S,
                            uint32_t* left, uint32_t* eq_total) {
   const int tid = threadIdx.x, w = tid / kWave;
+  // the first pass's histogram and compaction counter are cleared before the
+  // barrier that publishes the range
+  for (int i = tid; i < 2048; i += kNT) S.h[i] = 0u;
+  if (tid == 0) S.bc[2] = 0u;
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int u = 0; u < NPER; ++u)
@@ -730,9 +734,12 @@ CLSA_DEV uint32_t kth_regs(const uint32_t (&k)[NPER], int cnt, uint32_t rank, Se
   int shift = range < 2048u ? 0 : (32 - __clz(range)) - 11;
   int shift_prev = 32;
   uint32_t prefix = 0;  // (key - lo) >> shift_prev of the keys still in play
-  for (;;) {
-    for (int i = tid; i < 2048; i += kNT) S.h[i] = 0u;
-    __syncthreads();
+  for (bool first = true;; first = false) {
+    if (!first) {
+      for (int i = tid; i < 2048; i += kNT) S.h[i] = 0u;
+      if (tid == 0) S.bc[2] = 0u;
+      __syncthreads();
+    }
 #pragma unroll
     for (int u = 0; u < NPER; ++u)
       if (u < cnt) {
@@ -752,8 +759,6 @@ CLSA_DEV uint32_t kth_regs(const uint32_t (&k)[NPER], int cnt, uint32_t rank, Se
       return lo + full;
     }
     if (c <= (uint32_t)kSmall) {
-      if (tid == 0) S.bc[2] = 0u;
-      __syncthreads();
 #pragma unroll
       for (int u = 0; u < NPER; ++u)
         if (u < cnt && ((k[u] - lo) >> shift) == full) S.small[atomicAdd(&S.bc[2], 1u)] = k[u];
@@ -844,6 +849,11 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
     for (int64_t i = tid; i < n_vis; i += kNT) out[i] = (int32_t)i;
     return;
   }
+  // the selection bitmap is cleared now; the barriers of the k-th search
+  // order it before the marking
+  const int wpt = select_words_per_thread(a.n_cap);  // bitmap words per thread, contiguous
+  const int w0 = tid * wpt;
+  for (int i = w0; i < w0 + wpt; i += 4) bitmap4[i / 4] = u32x4_t{0u, 0u, 0u, 0u};
 
   // offsets of the row's segments (one per key chunk)
   const int nseg = CONTIG ? 1 : a.nchunks;
@@ -915,10 +925,6 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
 
   // mark the selection: keys above kstar, and of the keys equal to it the
   // `left` lowest positions
-  const int wpt = select_words_per_thread(a.n_cap);  // bitmap words per thread, contiguous
-  const int w0 = tid * wpt;
-  for (int i = w0; i < w0 + wpt; i += 4) bitmap4[i / 4] = u32x4_t{0u, 0u, 0u, 0u};
-  __syncthreads();
   if (left == eq_total) {
 #pragma unroll
     for (int u = 0; u < kPerT; ++u)
