@@ -80,17 +80,18 @@ CLSA_DEV void emit(const AttnArgs& a, int l, int r, int s, int nsplit, int h, in
 // ================================================================ combine
 // out = sum_s acc_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*), m* = max_s m_s;
 // lse = (m* + log2 sum_s l_s 2^(m_s - m*)) ln 2.  Rows with one split were
-// finished by their only workgroup.
+// finished by their only workgroup.  One wave per (head, row, layer): a row
+// of one sequence has Hq x L of them, enough to spread over the chip.
+constexpr int kCombineThreads = 64;
 template <typename T>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  const int r = blockIdx.x, l = blockIdx.y;
+__global__ __launch_bounds__(kCombineThreads) void attn_combine(AttnArgs a) {
+  const int h = blockIdx.x, r = blockIdx.y, l = blockIdx.z;
   const int nsplit = row_splits(a, row_count(a, r));
   if (nsplit == 1) return;
   const size_t base = ((size_t)l * a.B * a.M + r) * a.S;
-  for (int i = threadIdx.x; i < a.Hq * a.D; i += blockDim.x) {
-    const int h = i / a.D, d = i % a.D;
-    float ms = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, a.pml[(base + s) * a.Hq + h].x);
+  float ms = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, a.pml[(base + s) * a.Hq + h].x);
+  for (int d = threadIdx.x; d < a.D; d += kCombineThreads) {
     float L = 0.f, o = 0.f;
     if (ms != -INFINITY) {
       for (int s = 0; s < nsplit; ++s) {
@@ -586,9 +587,9 @@ extern "C" int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D,
     hipLaunchKernelGGL(attn_generic<float>, grid, dim3(256), 0, s, a);
   }
   if (p.S > 1) {
-    const dim3 cg((unsigned)R, (unsigned)L);
-    if (dt == CLSA_BF16) hipLaunchKernelGGL(attn_combine<uint16_t>, cg, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attn_combine<float>, cg, dim3(256), 0, s, a);
+    const dim3 cg((unsigned)Hq, (unsigned)R, (unsigned)L);
+    if (dt == CLSA_BF16) hipLaunchKernelGGL(attn_combine<uint16_t>, cg, dim3(kCombineThreads), 0, s, a);
+    else hipLaunchKernelGGL(attn_combine<float>, cg, dim3(kCombineThreads), 0, s, a);
   }
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
 }
