@@ -81,31 +81,61 @@ CLSA_DEV void emit(const AttnArgs& a, int l, int r, int s, int nsplit, int h, in
 // out = sum_s acc_s 2^(m_s - m*) / sum_s l_s 2^(m_s - m*), m* = max_s m_s;
 // lse = (m* + log2 sum_s l_s 2^(m_s - m*)) ln 2.  Rows with one split were
 // finished by their only workgroup.  One wave per (head, row, layer): a row
-// of one sequence has Hq x L of them, enough to spread over the chip.
+// of one sequence has Hq x L of them, enough to spread over the chip.  The
+// partials of kCombineGroup splits are loaded together and folded into a
+// running maximum and sums, so a row waits on memory once per group.
 constexpr int kCombineThreads = 64;
+constexpr int kCombineGroup = 8;
+constexpr int kCombineDims = 256 / kCombineThreads;  // head dims per lane, D <= 256
 template <typename T>
 __global__ __launch_bounds__(kCombineThreads) void attn_combine(AttnArgs a) {
   const int h = blockIdx.x, r = blockIdx.y, l = blockIdx.z;
   const int nsplit = row_splits(a, row_count(a, r));
   if (nsplit == 1) return;
   const size_t base = ((size_t)l * a.B * a.M + r) * a.S;
-  float ms = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) ms = fmaxf(ms, a.pml[(base + s) * a.Hq + h].x);
-  for (int d = threadIdx.x; d < a.D; d += kCombineThreads) {
-    float L = 0.f, o = 0.f;
-    if (ms != -INFINITY) {
-      for (int s = 0; s < nsplit; ++s) {
-        const float2 ml = a.pml[(base + s) * a.Hq + h];
-        const float wgt = (ml.x == -INFINITY) ? 0.f : exp2f(ml.x - ms);
-        L = fmaf(ml.y, wgt, L);
-        o = fmaf(a.pacc[((base + s) * a.Hq + h) * a.D + d], wgt, o);
+  const int t = threadIdx.x;
+  float m = -INFINITY, L = 0.f, o[kCombineDims];
+#pragma unroll
+  for (int i = 0; i < kCombineDims; ++i) o[i] = 0.f;
+  for (int s0 = 0; s0 < nsplit; s0 += kCombineGroup) {
+    float2 ml[kCombineGroup];
+    float pa[kCombineGroup][kCombineDims];
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const int s = s0 + u;
+      const size_t p = (base + s) * a.Hq + h;
+      ml[u] = s < nsplit ? a.pml[p] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+      for (int i = 0; i < kCombineDims; ++i) {
+        const int d = t + i * kCombineThreads;
+        pa[u][i] = (s < nsplit && d < a.D) ? a.pacc[p * a.D + d] : 0.f;
       }
     }
-    const float res = L > 0.f ? o / L : 0.f;
-    static_cast<T*>(a.out[l])[((size_t)r * a.Hq + h) * a.D + d] = from_f32<T>(res);
-    if (d == 0 && a.lse)
-      a.lse[((size_t)l * a.B * a.M + r) * a.Hq + h] = L > 0.f ? (ms + __log2f(L)) * kLn2 : -INFINITY;
+    float mg = m;
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) mg = fmaxf(mg, ml[u].x);
+    if (mg == -INFINITY) continue;  // nothing attended so far
+    const float keep = m == -INFINITY ? 0.f : exp2f(m - mg);
+    L *= keep;
+#pragma unroll
+    for (int i = 0; i < kCombineDims; ++i) o[i] *= keep;
+#pragma unroll
+    for (int u = 0; u < kCombineGroup; ++u) {
+      const float w = ml[u].x == -INFINITY ? 0.f : exp2f(ml[u].x - mg);
+      L = fmaf(ml[u].y, w, L);
+#pragma unroll
+      for (int i = 0; i < kCombineDims; ++i) o[i] = fmaf(pa[u][i], w, o[i]);
+    }
+    m = mg;
   }
+#pragma unroll
+  for (int i = 0; i < kCombineDims; ++i) {
+    const int d = t + i * kCombineThreads;
+    if (d < a.D)
+      static_cast<T*>(a.out[l])[((size_t)r * a.Hq + h) * a.D + d] = from_f32<T>(L > 0.f ? o[i] / L : 0.f);
+  }
+  if (t == 0 && a.lse)
+    a.lse[((size_t)l * a.B * a.M + r) * a.Hq + h] = L > 0.f ? (m + __log2f(L)) * kLn2 : -INFINITY;
 }
 
 // ======================================================= gathered (bf16)
