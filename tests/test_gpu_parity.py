@@ -316,6 +316,30 @@ def test_attn_out_of_range_entries_are_skipped():
         assert np.max(np.abs(f64(out[0, 0, m]) - o_out[0, 0, 0])) <= 2e-2
 
 
+def test_attn_split_rows_with_empty_splits():
+    # one query row per layer is split 8 ways (256 entries each); in row 0
+    # the second half of the list is -1, so four splits hold nothing and the
+    # merge must ignore them; row 1 holds only -1 entries (out 0, lse -inf)
+    q, K, V, idx, counts = _attn_case(torch.bfloat16, 2, 1, 2, 32, 8, 128, 5000, 2048, [2048],
+                                      28)
+    idx[0, 0, 1024:] = -1
+    idx[0, 1, :] = -1
+    out, lse = clsa.sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), counts.to(DEV),
+                                want_lse=True)
+    # the oracle takes the valid entries only: row 0's first 1024, none of row 1's
+    o_cnt = counts.numpy().copy()
+    o_cnt[0, 0], o_cnt[0, 1] = 1024, 0
+    o_out, o_lse = O.sparse_attn([f64(q[l]) for l in range(2)], [f64(K[l]) for l in range(2)],
+                                 [f64(V[l]) for l in range(2)], idx.numpy(), o_cnt, 2048)
+    assert np.max(np.abs(f64(out) - o_out)) <= ATOL[torch.bfloat16]
+    gl = f64(lse)
+    assert np.all(np.isneginf(gl[:, 0, 1])) and np.all(np.isneginf(o_lse[:, 0, 1]))
+    assert np.all(f64(out)[:, 0, 1] == 0.0)
+    fin = np.isfinite(o_lse)
+    assert np.array_equal(np.isfinite(gl), fin)
+    assert np.max(np.abs(gl[fin] - o_lse[fin])) <= 1e-3
+
+
 def test_attn_split_and_single_pass_agree():
     # one row per layer is split across workgroups; 4096 rows are not
     q, K, V, idx, counts = _attn_case(torch.bfloat16, 1, 1, 1, 32, 8, 128, 8000, 2048, [2048], 27)
