@@ -5,19 +5,22 @@
 // positions, produced once per query token.
 //
 // Grid: (split, row, layer).  A split is TS consecutive entries of the row's
-// index list; each workgroup streams its entries in sub-blocks of 64
-// tokens with an online (running max / running sum) softmax and writes
-// either the final output (one split) or a partial (m, l, acc) that
-// attn_combine merges with the log-sum-exp rule.  No workgroup waits for
-// another; the kernel boundary orders the merge.
+// index list; its workgroup writes either the final output (one split) or
+// a partial (m, l, acc) that attn_combine merges with the log-sum-exp rule.
+// No workgroup waits for another; the kernel boundary orders the merge.
 //
 // attn_bf16  (bf16, D = 64/128/256, Hq/Hkv in {1,2,4,8,16}): one workgroup per
-//            KV head and split, four waves over its tokens.  Every gathered K
-//            and V row is read once, as whole cache lines, and used by all G
-//            query heads of its KV head.  This is an HBM-bound gather (about
-//            4 flop per byte), so the dot products run on the VALU
-//            (v_dot2_f32_bf16) rather than being padded into MFMA tiles.
-// attn_generic (fp32, or shapes attn_bf16 does not take): plain VALU.
+//            KV head and split, four waves over its tokens, in three phases:
+//            all scores of the split, an exact softmax over them, then P.V.
+//            Every gathered K and V row is read once, as whole cache lines,
+//            and used by all G query heads of its KV head.  This is an
+//            HBM-bound gather (about 4 flop per byte), so the dot products
+//            run on the VALU (v_dot2_f32_bf16) rather than being padded into
+//            MFMA tiles.  Loads carry the streaming hint unless the launch's
+//            rows share positions (attn_streaming).
+// attn_generic (fp32, or shapes attn_bf16 does not take): plain VALU, in
+//            sub-blocks of 64 tokens with an online (running max / running
+//            sum) softmax.
 #include "clsa_common.h"
 
 namespace clsa {
