@@ -276,7 +276,25 @@ void attn_bf16(AttnArgs a) {
       }
     }
   }
-  __syncthreads();
+  // The wave's first batch of V rows goes out now and arrives during the
+  // softmax rather than after it.  The barriers around the softmax publish
+  // LDS only (scores, then probabilities), so they leave these loads in
+  // flight.
+  auto load_v = [&](int grp0, u32x4_t (&vv)[kVB], int (&ts)[kVB], int (&rws)[kVB]) {
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int t = (grp0 + u) * kTPW + tq;
+      const int rw = t < nt ? sidx[t] : -1;
+      ts[u] = t;
+      rws[u] = rw;
+      vv[u] = load_row16<NT>(Vl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
+    }
+  };
+  u32x4_t vv0[kVB];
+  int ts0[kVB], rws0[kVB];
+  const bool first_v = w * kVB < ngroups;  // wave-uniform
+  if (first_v) load_v(w * kVB, vv0, ts0, rws0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // ---- phase B: softmax per head over the split; wave w owns heads
   //      w, w+4, ... and keeps their max and sum in registers ----
@@ -300,7 +318,7 @@ void attn_bf16(AttnArgs a) {
     hm[i] = mx;
     hl[i] = sum;
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // ---- phase C: P.V (skipped rows have p = 0) ----
   float acc[G][8];
@@ -308,17 +326,7 @@ void attn_bf16(AttnArgs a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  for (int grp0 = w * kVB; grp0 < ngroups; grp0 += kWaves * kVB) {
-    u32x4_t vv[kVB];
-    int ts[kVB], rws[kVB];
-#pragma unroll
-    for (int u = 0; u < kVB; ++u) {
-      const int t = (grp0 + u) * kTPW + tq;
-      const int rw = t < nt ? sidx[t] : -1;
-      ts[u] = t;
-      rws[u] = rw;
-      vv[u] = load_row16<NT>(Vl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
-    }
+  auto fold_v = [&](const u32x4_t (&vv)[kVB], const int (&ts)[kVB], const int (&rws)[kVB]) {
 #pragma unroll
     for (int u = 0; u < kVB; ++u) {
       float vf[8];
@@ -334,6 +342,13 @@ void attn_bf16(AttnArgs a) {
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
       }
     }
+  };
+  if (first_v) fold_v(vv0, ts0, rws0);
+  for (int grp0 = w * kVB + kWaves * kVB; grp0 < ngroups; grp0 += kWaves * kVB) {
+    u32x4_t vv[kVB];
+    int ts[kVB], rws[kVB];
+    load_v(grp0, vv, ts, rws);
+    fold_v(vv, ts, rws);
   }
   // sum the token slots sharing a dim slice, then the 4 waves (in LDS)
 #pragma unroll
