@@ -422,8 +422,9 @@ def main():
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(sequences shard across GPUs with no exchange; see the design notes)",
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
+              "(decode sequences would shard across GPUs with no exchange, each GPU "
+              "running this path on its share)",
               file=sys.stderr)
         sys.exit(2)
 
