@@ -25,8 +25,8 @@ Sources (the pages this follows):
     threshold tau defines the half-space {p : <q, p> >= tau}, and the answer
     is every key inside it (no false negatives).
 
-Readings where the pages are silent (each one is listed with its reason in
-the design notes of the repository):
+Readings where the pages are silent (the plainest reading the rest of the
+pages supports):
 
 * R1/R2  the routing score is the raw inner product q_idx . K_idx[j] with no
          scale and no nonlinearity (one index head);
