@@ -523,19 +523,11 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
     uint32_t pw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) pw[q] = (uint32_t)(jl0 + idx[q] + (idx[q] & 28));
-    // exactly the pass's n entries (the partner lane's follow them): pairs
-    // as 16-byte stores, an odd last one as 8 bytes
+    // exactly the pass's n entries (the partner lane's follow them)
     uint64_t* dst = st.segp + at;
-    if (n >= 2u)
-      reinterpret_cast<u32x4_t*>(dst)[0] =
-          u32x4_t{pw[0], __float_as_uint(dv[0]), pw[1], __float_as_uint(dv[1])};
-    else if (n == 1u)
-      dst[0] = ((uint64_t)__float_as_uint(dv[0]) << 32) | pw[0];
-    if (n == 4u)
-      reinterpret_cast<u32x4_t*>(dst)[1] =
-          u32x4_t{pw[2], __float_as_uint(dv[2]), pw[3], __float_as_uint(dv[3])};
-    else if (n == 3u)
-      dst[2] = ((uint64_t)__float_as_uint(dv[2]) << 32) | pw[2];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if ((uint32_t)q < n) dst[q] = ((uint64_t)__float_as_uint(dv[q]) << 32) | pw[q];
     st.gcnt += pair_total;
     hits = h;
   }
