@@ -150,3 +150,16 @@ def test_binding_fails_loudly_without_library(tmp_path):
     from long_context_sparse_routing_amd import binding
     with pytest.raises(RuntimeError, match="not found"):
         binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    # the benchmark measures one GPU; asking for more exits with status 2
+    # and says why, before touching any device
+    import subprocess
+    import sys
+    from pathlib import Path
+    root = Path(__file__).resolve().parents[1]
+    res = subprocess.run([sys.executable, str(root / "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=120)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
