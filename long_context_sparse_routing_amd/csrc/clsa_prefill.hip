@@ -103,13 +103,17 @@ CLSA_DEV void load_q_slab(const BlockArgs& a, int b, int m0, bf16x8_t (&qa)[D / 
   }
 }
 
-// Staged keys in LDS: key n holds D/8 16-byte pieces; piece c sits in slot
-// c ^ (n % (D/8)), so 32 lanes reading one piece of 32 keys spread over the
-// banks.
+// Staged keys in LDS: key n holds P = D/8 16-byte pieces; piece c sits in
+// slot c ^ ((n / (16/P)) % P).  LDS serves 16 lanes x 16 bytes per clock
+// from 64 banks, so the 16 lanes reading one piece of 16 consecutive keys
+// must cover 16 distinct 16-byte bank groups: the keys' rows fix the group
+// modulo 16/P, the slot swizzle the rest.
 template <int D>
 CLSA_DEV int lds_piece(int n, int c) {
   constexpr int P = D / 8;
-  return n * P + (c ^ (n & (P - 1)));
+  constexpr int kShift = P >= 16 ? 0 : (P == 8 ? 1 : 2);
+  static_assert(P == 4 || P == 8 || P == 16, "d_idx 32, 64 or 128");
+  return n * P + (c ^ ((n >> kShift) & (P - 1)));
 }
 
 template <int D>
@@ -435,9 +439,10 @@ __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
 // that keep every key (threshold -inf) and tiles crossing a row's
 // visibility limit take explicit compares instead.
 constexpr int kScrStride = 32;  // scratch words per lane: the step's 32 values
-// 16-byte piece q of a lane's scratch sits in slot q ^ (lane & 7), so the 8
-// lanes a 128-bit LDS access serves at once hit distinct banks.
-CLSA_DEV int scr_slot(int q, int lane) { return q ^ (lane & 7); }
+// 16-byte piece q of a lane's scratch sits in slot q ^ ((lane / 2) % 8):
+// a lane's 128 bytes fill half of the 64 banks, so the 16 lanes a 128-bit
+// LDS access serves at once hit 16 distinct bank groups.
+CLSA_DEV int scr_slot(int q, int lane) { return q ^ ((lane >> 1) & 7); }
 
 // bf16 bits of -x, with x first rounded down to bf16 (toward -inf)
 CLSA_DEV uint16_t neg_bf16_floor(float x) {
@@ -501,7 +506,7 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
       reinterpret_cast<float4*>(scr)[scr_slot(4 + q, lane)] =
           make_float4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3]);
   }
-  const int sw = (lane & 7) << 2;  // word i of the lane's values sits at i ^ sw
+  const int sw = ((lane >> 1) & 7) << 2;  // word i of the lane's values sits at i ^ sw
   while (__ballot(hits != 0u) != 0) {
     int idx[4];
     float dv[4];
@@ -617,6 +622,10 @@ void block_filter(BlockArgs a) {
       bf16x8_t kb0[D / 16], kb1[D / 16];
       load_k_tile<D>(kc, 2 * sidx, kb0);
       load_k_tile<D>(kc, 2 * sidx + 1, kb1);
+      // all of the step's key reads go out before its first MFMA (left to
+      // itself the scheduler feeds each MFMA its own just-in-time read, one
+      // LDS round trip per k-step)
+      __builtin_amdgcn_sched_barrier(0);
       // rows: keys, columns: queries; the last k-step subtracts T'
       f32x16_t x0 = tile_mma<D>(kb0, qb, f32x16_t{});
       f32x16_t x1 = tile_mma<D>(kb1, qb, f32x16_t{});
