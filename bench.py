@@ -68,6 +68,84 @@ def route_bytes(B, M, n, d, k, esize=2):
     return B * n * d * esize + B * M * d * esize + B * M * (k + 1) * 4
 
 
+def per_layer_launches(wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos_all,
+                       new_rows, steps, dev):
+    """The decode steps with attention launched layer by layer.
+
+    A model has layer l's query only after layer l-1's output, so a real
+    step is append + one routing call + L single-layer attention calls with
+    the rest of each layer in between.  Each step here is captured in two HIP
+    graphs (append + route, then the L attention calls) on a stream of its
+    own, so that the host's launch cost is not timed; the same calls run
+    eagerly first and every replay must reproduce them bit for bit."""
+    import torch
+    new_kidx, new_k, new_v = new_rows
+    total = len(q_all)
+    T = list(range(total - steps, total))
+    s = torch.cuda.Stream()
+    idx = torch.empty((wl.B, 1, wl.k), dtype=torch.int32, device=dev)
+    counts = torch.empty((wl.B, 1), dtype=torch.int32, device=dev)
+    out = torch.empty((wl.L, wl.B, 1, wl.Hq, wl.D), dtype=torch.bfloat16, device=dev)
+    ws_r = torch.empty(clsa.route_workspace_size(wl.B, 1, wl.d, wl.n_cap, wl.k, wl.k,
+                                                 torch.bfloat16), dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(max(1, clsa.sparse_attn_workspace_size(1, wl.B, 1, wl.Hq, wl.Hkv, wl.D,
+                                                              wl.k, torch.bfloat16)),
+                       dtype=torch.uint8, device=dev)
+    calls = []
+    for t in T:
+        pre = [clsa.prepare_kv_append(pos_all[t], new_kidx[t], K_idx, new_k[t], Kc, new_v[t], Vc,
+                                      stream=s),
+               clsa.prepare_route(q_idx_all[t], K_idx, wl.k, n_ctx=n_ctx_all[t], idx=idx,
+                                  counts=counts, ws=ws_r, stream=s)]
+        layers = [clsa.prepare_sparse_attn([q_all[t][l]], [Kc[l]], [Vc[l]], idx, counts,
+                                           out=[out[l]], ws=ws_l, stream=s)
+                  for l in range(wl.L)]
+        calls.append((pre, layers))
+    torch.cuda.synchronize()
+    # eager reference of the last step
+    with torch.cuda.stream(s):
+        for c in calls[-1][0] + calls[-1][1]:
+            c()
+    s.synchronize()
+    ref = (idx.clone(), out.clone())
+    graphs = []
+    for pre, layers in calls:
+        g1, g2 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g1, stream=s):
+            for c in pre:
+                c()
+        with torch.cuda.graph(g2, stream=s):
+            for c in layers:
+                c()
+        graphs.append((g1, g2))
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in T]
+    torch.cuda.synchronize()
+    for g1, g2 in graphs[:2]:  # warm the graphs
+        g1.replay()
+        g2.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(s):
+        for i, (g1, g2) in enumerate(graphs):
+            g1.replay()
+            ev[i][0].record(s)
+            g2.replay()
+            ev[i][1].record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    same = torch.equal(idx, ref[0]) and torch.equal(out, ref[1])
+    if not same:
+        raise RuntimeError("per-layer graph replay differs from its eager run")
+    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(T)
+    ms = wall * 1e3 / len(T)
+    return {"steps": len(T), "ms_per_step": ms, "tokens_per_s": wl.B * len(T) / wall,
+            "attn_ms_per_step": attn_ms, "attn_ms_per_layer": attn_ms / wl.L,
+            "replays_match_eager": same,
+            "note": "append + route + one clsa_sparse_attn call per layer, each step in two "
+                    "HIP graphs; the headline value launches the 16 layers' attention as one call"}
+
+
 def cpu_baseline(wl, K_idx, Kc, Vc, q_idx, q, n, budget_s):
     """Time the CPU oracle (as written) on a bounded sample of decode
     sequence-steps: routing over all n keys plus attention in all layers."""
@@ -418,6 +496,8 @@ def main():
                     help="timed calls of the prefill-chunk routing leg (0: skip)")
     ap.add_argument("--prefill-attention", type=int, default=1,
                     help="also time the prefill chunk's sparse attention (0: skip)")
+    ap.add_argument("--per-layer-steps", type=int, default=16,
+                    help="decode steps timed again with one attention call per layer (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
@@ -552,6 +632,10 @@ def main():
                            "frac": r_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                            "algorithmic_bytes_per_call": r_bytes},
     }
+    if args.per_layer_steps > 0:
+        res["per_layer_launches"] = per_layer_launches(
+            wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos_all,
+            (new_kidx, new_k, new_v), min(args.per_layer_steps, total_steps), dev)
     if args.baseline_steps > 0:
         res["baselines"] = baselines(wl, Kc, Vc, q_all[total_steps - 1], N0 + total_steps, dev,
                                      args.baseline_steps, ms_step)
