@@ -146,51 +146,73 @@ def per_layer_launches(wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos
                     "HIP graphs; the headline value launches the 16 layers' attention as one call"}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def oracle_decode_rate(wl, K_idx, Kc, Vc, q_idx, q, n_vis, select, budget_s, order=None,
+                       threads=None):
+    """Time the CPU oracle (as written) on decode sequence-steps of one
+    workload: fp64 routing scores over the sequence's visible keys, the
+    selection select(b, scores), then attention in every layer and head over
+    the selected rows.  Sequences are taken in `order` until the budget is
+    spent; host copies of the inputs happen before each clock starts.
+    threads=1 pins the BLAS pool to one thread."""
+    import contextlib
+    import numpy as np
+    import torch
+    from oracle import clsa_oracle as O
+    limit = contextlib.nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        limit = threadpool_limits(limits=threads)
+    with limit:
+        used = _blas_threads()
+        q_np = q_idx.double().cpu().numpy()
+        qa = [q[l].double().cpu().numpy() for l in range(wl.L)]
+        sc = 1.0 / math.sqrt(wl.D)
+        G = wl.Hq // wl.Hkv
+        done, t_tot, seqs = 0, 0.0, []
+        for b in (order if order is not None else range(wl.B)):
+            n = n_vis(b)
+            K_np = K_idx[b, :n].double().cpu().numpy()
+            t0 = time.perf_counter()
+            sel = select(b, O.route_scores(q_np[b, 0], K_np, n))
+            t_route = time.perf_counter() - t0
+            selt = torch.from_numpy(np.asarray(sel, dtype=np.int64)).to(Kc.device)
+            Kr = [Kc[l, b][selt].double().cpu().numpy() for l in range(wl.L)]
+            Vr = [Vc[l, b][selt].double().cpu().numpy() for l in range(wl.L)]
+            t0 = time.perf_counter()
+            for l in range(wl.L):
+                for h in range(wl.Hq):
+                    O.attend_head(qa[l][b, 0, h], Kr[l][:, h // G, :], Vr[l][:, h // G, :], sc)
+            t_tot += t_route + time.perf_counter() - t0
+            done += 1
+            seqs.append(b)
+            if t_tot >= budget_s:
+                break
+    return done, t_tot, used, seqs
+
+
 def cpu_baseline(wl, K_idx, Kc, Vc, q_idx, q, n, budget_s):
     """Time the CPU oracle (as written) on a bounded sample of decode
     sequence-steps: routing over all n keys plus attention in all layers."""
-    import numpy as np
     from oracle import clsa_oracle as O
-
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        blas_threads = 1
     affinity = len(os.sched_getaffinity(0))
-    # host copies are input preparation, done before the clock starts
-    K_np = [K_idx[b, :n].double().cpu().numpy() for b in range(wl.B)]
-    q_np = q_idx.double().cpu().numpy()
-    qa = [q[l].double().cpu().numpy() for l in range(wl.L)]
-    done, t_tot = 0, 0.0
-    for b in range(wl.B):
-        t0 = time.perf_counter()
-        s = O.route_scores(q_np[b, 0], K_np[b], n)
-        sel = O.topk_select(s, wl.k)
-        t_route = time.perf_counter() - t0
-        import torch
-        selt = torch.from_numpy(sel).to(Kc.device)
-        Kr = [Kc[l, b][selt].double().cpu().numpy() for l in range(wl.L)]
-        Vr = [Vc[l, b][selt].double().cpu().numpy() for l in range(wl.L)]
-        t0 = time.perf_counter()
-        sc = 1.0 / math.sqrt(wl.D)
-        G = wl.Hq // wl.Hkv
-        for l in range(wl.L):
-            for h in range(wl.Hq):
-                O.attend_head(qa[l][b, 0, h], Kr[l][:, h // G, :], Vr[l][:, h // G, :], sc)
-        t_attn = time.perf_counter() - t0
-        t_tot += t_route + t_attn
-        done += 1
-        if t_tot >= budget_s:
-            break
+    done, t_tot, used, _ = oracle_decode_rate(
+        wl, K_idx, Kc, Vc, q_idx, q, lambda b: n, lambda b, s: O.topk_select(s, wl.k), budget_s)
     return {
         "value": done / t_tot,
         "unit": "tokens/s",
-        "cores": blas_threads,
+        "cores": used,
         "kind": "oracle",
         "sample": (f"{done} sequence-steps of {wl.name} (one decode token each: fp64 routing "
                    f"over {n} keys, exact top-{wl.k}, attention in {wl.L} layers x {wl.Hq} "
-                   f"heads); NumPy BLAS threads={blas_threads}, affinity cpus={affinity}"),
+                   f"heads); NumPy BLAS threads={used}, affinity cpus={affinity}"),
     }
 
 
@@ -231,9 +253,7 @@ def prefill_routing(calls, dev, cpu_budget, with_attention=True):
     K_idx, u, _ = gen.gen_routing_keys(wl, dev)
     q_idx = gen.gen_routing_query(wl, u, 0, dev)
     call = clsa.prepare_route(q_idx, K_idx, wl.k, q_pos0=wl.q_pos0)
-    for _ in range(3):
-        call()
-    torch.cuda.synchronize()
+    _settle(call)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(calls):
@@ -310,8 +330,7 @@ def baselines(wl, Kc, Vc, q, n, dev, steps, shared_ms):
     from long_context_sparse_routing_amd import inputs as gen
 
     def timed(fn):
-        for _ in range(2):
-            fn()
+        _settle(fn)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -362,9 +381,25 @@ def baselines(wl, Kc, Vc, q, n, dev, steps, shared_ms):
     }
 
 
+def _settle(fn, min_ms=25.0):
+    """Repeat fn until the GPU has run it for at least min_ms: the clocks
+    are at their working level before timing starts (a few calls after the
+    host-side input preparation measure several percent slow)."""
+    import torch
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while True:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+            if (time.perf_counter() - t0) * 1e3 >= min_ms:
+                return
+
+
 def _event_ms(fn, reps):
     import torch
-    fn()
+    _settle(fn)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -394,7 +429,7 @@ def _mall_cold_ms(calls):
     return sum(a.elapsed_time(b) for a, b in evs) / len(evs)
 
 
-def threshold_step(dev, reps):
+def threshold_step(dev, reps, cpu_budget=0.0):
     """Half-space selection at 128K: 16 sequences, d_idx 128, per-sequence
     tau set so that 256 .. 8192 keys qualify (Louver summary, section on the
     half-space reduction), then attention over those lists in 16 layers."""
@@ -418,9 +453,19 @@ def threshold_step(dev, reps):
     scan = wl.B * wl.n_ctx * wl.d * 2
     gather = sel * wl.L * wl.Hkv * wl.D * 2 * 2
     step_bytes = scan + gather + 2 * q.numel() * 2
+    cpu = None
+    if cpu_budget > 0:
+        from oracle import clsa_oracle as O
+        order = [int(f"{b:04b}"[::-1], 2) for b in range(wl.B)]  # spread over the count range
+        done, tt, used, seqs = oracle_decode_rate(
+            wl, K_idx, Kc, Vc, q_idx, q, lambda b: wl.n_ctx,
+            lambda b, sc_: O.threshold_select(sc_, float(tau[b])), cpu_budget, order=order)
+        cpu = {"value": done / tt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+               "sample": (f"sequences {seqs} of {wl.name} (fp64 scores over {wl.n_ctx} keys, "
+                          f"threshold selection, attention in {wl.L} layers x {wl.Hq} heads)")}
     del Kc, Vc, q, attn, route, K_idx
     torch.cuda.empty_cache()
-    return {"workload": wl.name, "sequences": wl.B, "selected_total": sel,
+    return {"workload": wl.name, "sequences": wl.B, "selected_total": sel, "cpu_baseline": cpu,
             "route_call_ms": route_ms, "attn_call_ms": attn_ms, "ms_per_step": step_ms,
             "tokens_per_s": wl.B / (step_ms * 1e-3),
             "route_roofline": {"bound": "hbm", "achieved": scan / (route_ms * 1e-3) / 1e9,
@@ -429,7 +474,7 @@ def threshold_step(dev, reps):
             "step_hbm_frac": step_bytes / (step_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
 
-def decode_32k_step(dev, steps):
+def decode_32k_step(dev, steps, cpu_budget=0.0):
     """One sequence at 32K context: append + route + attention in 16 layers,
     the single-sequence case where attention lists are split across
     workgroups and merged."""
@@ -455,6 +500,7 @@ def decode_32k_step(dev, steps):
     for t in range(2):
         for c in calls[t]:
             c()
+    _settle(lambda: [c() for c in calls[1]])  # step 1 again: its append rewrites one row
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -470,10 +516,20 @@ def decode_32k_step(dev, steps):
     n_mid = N0 + 2 + steps // 2
     step_bytes = (n_mid * wl.d * 2 + wl.L * wl.k * wl.Hkv * wl.D * 2 * 2
                   + 2 * wl.L * wl.Hq * wl.D * 2)
+    cpu = None
+    if cpu_budget > 0:
+        from oracle import clsa_oracle as O
+        t, cpu = T - 1, {}
+        for name, threads in (("all_cores", None), ("single_thread", 1)):
+            done, tt, used, _ = oracle_decode_rate(
+                wl, K_idx, Kc, Vc, qi[t], qa[t], lambda b: N0 + t + 1,
+                lambda b, sc_: O.topk_select(sc_, wl.k), cpu_budget, threads=threads)
+            cpu[name] = {"value": done / tt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+                         "sample": f"{done} decode step at n = {N0 + t + 1}"}
     del Kc, Vc, K_idx, calls
     torch.cuda.empty_cache()
     return {"workload": wl.name, "steps": steps, "ms_per_step": ms,
-            "tokens_per_s": 1.0 / (ms * 1e-3), "bytes_per_step": step_bytes,
+            "tokens_per_s": 1.0 / (ms * 1e-3), "bytes_per_step": step_bytes, "cpu_baseline": cpu,
             "step_hbm_frac": step_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
             "mall_cold": {"ms_per_step": cold_ms,
                           "step_hbm_frac": step_bytes / (cold_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
@@ -484,7 +540,7 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=64)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=64)
     ap.add_argument("--workload", default="decode_128k_b8")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of CPU oracle work in the baseline sample (0 = skip)")
@@ -496,6 +552,8 @@ def main():
                     help="timed calls of the prefill-chunk routing leg (0: skip)")
     ap.add_argument("--prefill-attention", type=int, default=1,
                     help="also time the prefill chunk's sparse attention (0: skip)")
+    ap.add_argument("--repeats", type=int, default=5,
+                    help="runs of --steps fresh decode steps in 'repeats' (value is the first)")
     ap.add_argument("--per-layer-steps", type=int, default=16,
                     help="decode steps timed again with one attention call per layer (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -525,7 +583,10 @@ def main():
         return
     clsa.load_library()
     base = gen.WORKLOADS[args.workload]
-    total_steps = args.warmup + args.steps
+    # warmup, the timed run, then args.repeats - 1 more runs of fresh steps
+    # (the decode simply continues), each args.steps long
+    n_runs = max(1, args.repeats)
+    total_steps = args.warmup + args.steps * n_runs
     wl = base.with_(n_cap=base.n_ctx + total_steps)
     N0 = wl.n_ctx
 
@@ -562,37 +623,52 @@ def main():
     ev_attn = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(total_steps)]
 
+    # HIP events bracket the attention call on every 8th step of the timed
+    # run: each recorded pair adds a few microseconds to its step
+    ev_every = 8
+
     def step(t, timed):
+        mark = timed and (t - args.warmup) % ev_every == 0
         appends[t]()                 # append (the self-decoder's KV write)
         routes[t]()                  # one routing step shared by all layers
-        if timed:
+        if mark:
             ev_attn[t][0].record(stream)
         attns[t]()                   # sparse attention in all layers
-        if timed:
+        if mark:
             ev_attn[t][1].record(stream)
 
     for t in range(args.warmup):
         step(t, False)
     torch.cuda.synchronize()
+    t_end = args.warmup + args.steps  # the timed run: `value`
     t0 = time.perf_counter()
-    for t in range(args.warmup, total_steps):
+    for t in range(args.warmup, t_end):
         step(t, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert int(counts.min()) == wl.k and int(counts.max()) == wl.k
-    attn_ms = sum(a.elapsed_time(b) for a, b in ev_attn[args.warmup:]) / args.steps
+    # further runs over the next steps, no events: the spread of the rate
+    walls = [wall]
+    for r in range(1, n_runs):
+        t1 = time.perf_counter()
+        for t in range(t_end + (r - 1) * args.steps, t_end + r * args.steps):
+            step(t, False)
+        torch.cuda.synchronize()
+        walls.append(time.perf_counter() - t1)
+    marked = [ev_attn[t] for t in range(args.warmup, t_end)
+              if (t - args.warmup) % ev_every == 0]
+    attn_ms = sum(a.elapsed_time(b) for a, b in marked) / len(marked)
 
     # routing call duration, from a separate pass over the last steps' inputs
     # (kept out of the timed loop so its events do not add gaps there)
-    n_rt = min(8, total_steps)
-    ev_r = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_rt)]
+    n_rt = min(8, args.steps)
+    ev_r = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    ev_r[0].record(stream)
     for i in range(n_rt):
-        ev_r[i][0].record(stream)
-        routes[total_steps - n_rt + i]()
-        ev_r[i][1].record(stream)
+        routes[t_end - n_rt + i]()
+    ev_r[1].record(stream)
     torch.cuda.synchronize()
-    route_ms = sum(a.elapsed_time(b) for a, b in ev_r) / n_rt
+    route_ms = ev_r[0].elapsed_time(ev_r[1]) / n_rt
 
     ms_step = wall * 1e3 / args.steps
     tokens = wl.B * args.steps
@@ -620,9 +696,22 @@ def main():
                    "layers": wl.L, "d_idx": wl.d, "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "head_dim": wl.D, "append_per_step": 1},
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "repeats": {"runs": len(walls),
+                    "tokens_per_s_median": tokens / sorted(walls)[len(walls) // 2],
+                    "tokens_per_s_min": tokens / max(walls),
+                    "tokens_per_s_max": tokens / min(walls),
+                    "tokens_per_s_runs": [tokens / w for w in walls],
+                    "how": (f"{n_runs} runs of {args.steps} consecutive decode steps (the "
+                            "decode continues from run to run); value is the first run")},
         "step_breakdown_ms": {"route_call": route_ms, "attn_call": attn_ms,
                               "append_and_gaps": ms_step - route_ms - attn_ms,
-                              "route_call_source": "separate pass after the timed loop"},
+                              "route_call_source": ("separate pass after the timed loop: "
+                                                    "the run's last 8 routing calls back to back"),
+                              "attn_call_source": f"HIP events on every {ev_every}th timed step",
+                              "note": ("the parts come from separate instruments; an event pair "
+                                       "keeps the attention dispatch from overlapping the "
+                                       "routing call's tail, so the parts can sum above the "
+                                       "step")},
         "roofline": {"kernel": "attn_bf16<4,128,streaming> (one clsa_sparse_attn launch, 16 layers)",
                      "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
@@ -647,8 +736,9 @@ def main():
     del Kc, Vc, appends, routes, attns, q_all, q_idx_all, new_kidx, new_k, new_v, K_idx
     torch.cuda.empty_cache()
     if args.other_configs:
-        res["threshold_128k_b16"] = threshold_step(dev, 5)
-        res["decode_32k"] = decode_32k_step(dev, 64)
+        cb = min(3.0, args.cpu_budget)
+        res["threshold_128k_b16"] = threshold_step(dev, 5, cb)
+        res["decode_32k"] = decode_32k_step(dev, 64, cb)
     if args.prefill_calls > 0:
         res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget),
                                                  bool(args.prefill_attention))
