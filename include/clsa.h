@@ -46,7 +46,15 @@ extern "C" {
 /* Maximum number of layers one clsa_sparse_attn call accepts. */
 #define CLSA_MAX_LAYERS 64
 
+/* Element type of keys, queries and K/V.  A caller may pass any int: the
+ * calls reject values other than these two with CLSA_ERR_UNSUPPORTED_DTYPE.
+ * C++ gives the enum int as its underlying type so that such a value is
+ * well defined there too (in C every int already is). */
+#ifdef __cplusplus
+typedef enum clsa_dtype : int {
+#else
 typedef enum clsa_dtype {
+#endif
   CLSA_F32 = 0,  /* IEEE binary32 */
   CLSA_BF16 = 1  /* bfloat16, stored as uint16 bit patterns */
 } clsa_dtype;
