@@ -22,7 +22,9 @@
  *  - The caller owns every buffer.  The library allocates no device memory
  *    and keeps no state between calls; scratch space comes from the caller's
  *    workspace `ws` of at least the size returned by the matching
- *    *_workspace_size function (same shape arguments).
+ *    *_workspace_size function (same shape arguments).  A size of 0 means
+ *    either that the call needs no workspace (ws may then be NULL) or that
+ *    the call would reject the shapes.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronizing.  Calls that share
  *    one workspace must be ordered (same stream, or synchronized).
@@ -112,8 +114,8 @@ const char* clsa_status_string(int status);
  * is redone exactly (much slower, results unchanged).  Other rows (fp32, or
  * k > 2048) keep every key's score in the workspace (12 bytes per key).
  * Errors: CLSA_ERR_INVALID (null pointer, B/M/k < 1, d unsupported,
- * n_cap < 1, cap < k, B*M*n_cap too large), CLSA_ERR_UNSUPPORTED_DTYPE,
- * CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.
+ * n_cap outside [1, 2^31 - 1], B*M > 65535, cap < k),
+ * CLSA_ERR_UNSUPPORTED_DTYPE, CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.
  */
 size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, int k, int cap,
                                  clsa_dtype dt);
@@ -158,8 +160,9 @@ int clsa_route_threshold(const void* q_idx, const void* K_idx, int B, int M, int
  *          logits), or NULL.
  * Query head h reads KV head h / (Hq/Hkv) (grouped-query attention).
  * An empty list gives out = 0 and lse = -inf.
- * Constraints: 1 <= L <= CLSA_MAX_LAYERS, Hq % Hkv == 0, Hq/Hkv <= 16,
- * Hkv <= 64, Hq <= 64, 8 <= D <= 256 and D % 8 == 0, Hq*D <= 8192.
+ * Constraints: 1 <= L <= CLSA_MAX_LAYERS, B*M <= 65535, cap >= 1,
+ * Hq % Hkv == 0, Hq/Hkv <= 16, Hkv <= 64, Hq <= 64, 8 <= D <= 256 and
+ * D % 8 == 0, Hq*D <= 8192, scale finite and >= 0.
  * Errors: CLSA_ERR_INVALID, CLSA_ERR_UNSUPPORTED_DTYPE, CLSA_ERR_WORKSPACE,
  * CLSA_ERR_HIP.
  */
