@@ -155,13 +155,14 @@ def _blas_threads():
 
 
 def oracle_decode_rate(wl, K_idx, Kc, Vc, q_idx, q, n_vis, select, budget_s, order=None,
-                       threads=None):
+                       threads=None, max_steps=256):
     """Time the CPU oracle (as written) on decode sequence-steps of one
     workload: fp64 routing scores over the sequence's visible keys, the
     selection select(b, scores), then attention in every layer and head over
-    the selected rows.  Sequences are taken in `order` until the budget is
-    spent; host copies of the inputs happen before each clock starts.
-    threads=1 pins the BLAS pool to one thread."""
+    the selected rows.  Sequences are taken in `order`, round after round,
+    until the budget is spent (or max_steps sequence-steps); host copies of
+    the inputs happen before each clock starts.  threads=1 pins the BLAS
+    pool to one thread."""
     import contextlib
     import numpy as np
     import torch
@@ -177,7 +178,9 @@ def oracle_decode_rate(wl, K_idx, Kc, Vc, q_idx, q, n_vis, select, budget_s, ord
         sc = 1.0 / math.sqrt(wl.D)
         G = wl.Hq // wl.Hkv
         done, t_tot, seqs = 0, 0.0, []
-        for b in (order if order is not None else range(wl.B)):
+        order = list(order if order is not None else range(wl.B))
+        for i in range(max_steps):
+            b = order[i % len(order)]
             n = n_vis(b)
             K_np = K_idx[b, :n].double().cpu().numpy()
             t0 = time.perf_counter()
@@ -192,7 +195,8 @@ def oracle_decode_rate(wl, K_idx, Kc, Vc, q_idx, q, n_vis, select, budget_s, ord
                     O.attend_head(qa[l][b, 0, h], Kr[l][:, h // G, :], Vr[l][:, h // G, :], sc)
             t_tot += t_route + time.perf_counter() - t0
             done += 1
-            seqs.append(b)
+            if b not in seqs:
+                seqs.append(b)
             if t_tot >= budget_s:
                 break
     return done, t_tot, used, seqs
@@ -461,8 +465,9 @@ def threshold_step(dev, reps, cpu_budget=0.0):
             wl, K_idx, Kc, Vc, q_idx, q, lambda b: wl.n_ctx,
             lambda b, sc_: O.threshold_select(sc_, float(tau[b])), cpu_budget, order=order)
         cpu = {"value": done / tt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-               "sample": (f"sequences {seqs} of {wl.name} (fp64 scores over {wl.n_ctx} keys, "
-                          f"threshold selection, attention in {wl.L} layers x {wl.Hq} heads)")}
+               "sample": (f"{done} sequence-steps over sequences {seqs} of {wl.name} (fp64 "
+                          f"scores over {wl.n_ctx} keys, threshold selection, attention in "
+                          f"{wl.L} layers x {wl.Hq} heads)")}
     del Kc, Vc, q, attn, route, K_idx
     torch.cuda.empty_cache()
     return {"workload": wl.name, "sequences": wl.B, "selected_total": sel, "cpu_baseline": cpu,
@@ -472,6 +477,36 @@ def threshold_step(dev, reps, cpu_budget=0.0):
                                "unit": "GB/s", "frac": scan / (route_ms * 1e-3) / (HBM_PEAK_GBS * 1e9),
                                "algorithmic_bytes_per_call": scan},
             "step_hbm_frac": step_bytes / (step_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+
+
+def tiny_fp32_step(dev, reps, cpu_budget=0.0):
+    """The smallest configuration: one fp32 sequence at 4K context, d_idx 32,
+    one layer with one head of dim 64, k = 256 -- a routing call plus an
+    attention call, bound by launch latency rather than bytes."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+    wl = gen.WORKLOADS["tiny_fp32_4k"]
+    K_idx, u, _ = gen.gen_routing_keys(wl, dev)
+    Kc, Vc = gen.gen_kv(wl, dev)
+    q_idx = gen.gen_routing_query(wl, u, 0, dev)
+    q = gen.gen_attn_query(wl, q_idx, 0, dev)
+    route = clsa.prepare_route(q_idx, K_idx, wl.k)
+    idx, counts = route()
+    attn = clsa.prepare_sparse_attn(q, Kc, Vc, idx, counts)
+    ms = _event_ms(lambda: (route(), attn()), reps)
+    cpu = None
+    if cpu_budget > 0:
+        from oracle import clsa_oracle as O
+        cpu = {}
+        for name, threads in (("all_cores", None), ("single_thread", 1)):
+            done, tt, used, _ = oracle_decode_rate(
+                wl, K_idx, Kc, Vc, q_idx, q, lambda b: wl.n_ctx,
+                lambda b, sc_: O.topk_select(sc_, wl.k), cpu_budget, threads=threads)
+            cpu[name] = {"value": done / tt, "unit": "tokens/s", "cores": used, "kind": "oracle",
+                         "sample": f"{done} decode steps at n = {wl.n_ctx}"}
+    return {"workload": wl.name, "ms_per_step": ms, "tokens_per_s": 1.0 / (ms * 1e-3),
+            "what": "routing call + attention call, back to back", "cpu_baseline": cpu}
 
 
 def decode_32k_step(dev, steps, cpu_budget=0.0):
@@ -525,7 +560,7 @@ def decode_32k_step(dev, steps, cpu_budget=0.0):
                 wl, K_idx, Kc, Vc, qi[t], qa[t], lambda b: N0 + t + 1,
                 lambda b, sc_: O.topk_select(sc_, wl.k), cpu_budget, threads=threads)
             cpu[name] = {"value": done / tt, "unit": "tokens/s", "cores": used, "kind": "oracle",
-                         "sample": f"{done} decode step at n = {N0 + t + 1}"}
+                         "sample": f"{done} decode steps at n = {N0 + t + 1}"}
     del Kc, Vc, K_idx, calls
     torch.cuda.empty_cache()
     return {"workload": wl.name, "steps": steps, "ms_per_step": ms,
@@ -739,6 +774,7 @@ def main():
         cb = min(3.0, args.cpu_budget)
         res["threshold_128k_b16"] = threshold_step(dev, 5, cb)
         res["decode_32k"] = decode_32k_step(dev, 64, cb)
+        res["tiny_fp32_4k"] = tiny_fp32_step(dev, 200, min(1.0, cb))
     if args.prefill_calls > 0:
         res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget),
                                                  bool(args.prefill_attention))
