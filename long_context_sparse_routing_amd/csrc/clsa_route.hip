@@ -53,7 +53,7 @@ constexpr int kBuckets = 2048;    // histogram of the top 11 key bits
 constexpr int kBucketShift = 21;
 constexpr uint32_t kLowMask = (1u << kBucketShift) - 1u;
 constexpr int kMaxChunks = 4096;  // chunks per row
-constexpr int kMaxFilterCH = 1024;  // keys per chunk in filter mode (at most)
+constexpr int kMaxFilterCH = 2048;  // keys per chunk in filter mode (at most)
 
 // what route_score does with the scores
 constexpr int kHist = 0;    // top-k: keys + histogram of the top 11 bits
@@ -714,7 +714,8 @@ void launch_score(const RouteArgs& a, clsa_dtype dt, int d, dim3 grid, hipStream
 }
 
 // Filter path workspace: keys per chunk chosen so that the score pass has
-// about a thousand workgroups (256 .. 1024 keys, a multiple of the block);
+// at least about a thousand workgroups (256 .. 2048 keys, a multiple of the
+// block; 8 rows at 128K take 1024-key chunks, 32 rows 2048);
 // per row the samples, the candidate count and the candidate list.
 struct FilterLayout {
   int CH, C;

@@ -97,3 +97,20 @@ def test_many_sequences_one_launch():
     idx, counts = clsa.route(q.to(DEV), K.to(DEV), 1024, n_ctx=nc)
     torch.cuda.synchronize()
     _check(idx, counts, q, K, n_ctx, -1, 1024, 1024, rows=[(b, 0) for b in range(0, B, 3)])
+
+
+def test_many_sequences_take_the_longest_chunks():
+    # 32 sequences x 64K keys: enough rows for the score pass to take its
+    # longest chunks (2048 keys); ragged contexts end inside a chunk, on a
+    # chunk boundary and one key past it
+    g = _gen(900)
+    B, n = 32, 65536
+    n_ctx = [n - 977 * (b % 7) for b in range(B)]
+    n_ctx[3], n_ctx[4] = 6 * 2048, 6 * 2048 + 1
+    K = torch.randn((B, n, 64), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, 1, 64), generator=g) / 8).to(torch.bfloat16)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 2048, n_ctx=nc)
+    torch.cuda.synchronize()
+    for b in (0, 3, 4, 13, 31):  # one sequence at a time: the host copy stays small
+        _check(idx[b:b + 1], counts[b:b + 1], q[b:b + 1], K[b:b + 1], [n_ctx[b]], -1, 2048, 2048)
