@@ -140,18 +140,6 @@ CLSA_DEV uint32_t block_rank(bool p, uint32_t* wcnt, uint32_t* total) {
   return before + lanes_below(mask);
 }
 
-// ------------------------------------------------------------ memory order
-// Release this workgroup's prior global writes to the whole device, then
-// count one arrival on `ticket`; returns the previous count.
-CLSA_DEV uint32_t arrive_release(uint32_t* ticket) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  return __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-CLSA_DEV void acquire_device() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-CLSA_DEV uint32_t load_relaxed(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 __host__ __device__ inline int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------ sampled lower bound of the k-th score

@@ -134,9 +134,6 @@ CLSA_DEV f32x16_t tile_mma(const bf16x8_t (&x)[D / 16], const bf16x8_t (&y)[D / 
   return c;
 }
 
-// row of accumulator value v held by lane l (its column is l % 32)
-CLSA_DEV int acc_row(int v, int lane) { return 8 * (v / 4) + 4 * (lane / 32) + (v % 4); }
-
 // ----------------------------------------------------- LDS radix helpers
 // Bin holding the rank-th largest element of histogram h[0..NB) (bin NB-1
 // holds the largest values); rank is 1-based.  out2 = {bin, rank within}.
