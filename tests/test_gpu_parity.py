@@ -527,3 +527,41 @@ def test_kv_append_writes_each_sequence_slot():
         V0[:, b, p] = nv[:, b]
         Ki0[b, p] = ni[b]
     assert torch.equal(K, K0) and torch.equal(V, V0) and torch.equal(Ki, Ki0)
+
+
+def test_decode_steps_append_route_attend():
+    # the benchmark's step, three times in a row on a small decode shape:
+    # each step appends one row per sequence (its routing key, and K/V in
+    # every layer) with clsa_kv_append, routes over the grown context and
+    # attends.  Each step is checked against the oracle on the caches as
+    # that step left them.  One context grows through 4096 keys, where the
+    # routing sample starts to skip keys.
+    wl = gen.WORKLOADS["decode_32k"].with_(B=3, n_ctx=6000, n_cap=6008, L=3, k=1024,
+                                           planted=32)
+    K_idx, u, _ = gen.gen_routing_keys(wl, DEV)
+    Kc, Vc = gen.gen_kv(wl, DEV)
+    steps = 3
+    new_kidx, new_k, new_v = gen.gen_append_rows(wl, steps, DEV)
+    n0 = [6000, 5000, 4094]
+    for t in range(steps):
+        n_ctx = [n + t + 1 for n in n0]
+        pos = torch.tensor([n - 1 for n in n_ctx], dtype=torch.int32, device=DEV)
+        nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+        q_idx = gen.gen_routing_query(wl, u, t, DEV)
+        q = gen.gen_attn_query(wl, q_idx, t, DEV)
+        clsa.kv_append(pos, new_kidx[t], K_idx, new_k[t], Kc, new_v[t], Vc)
+        idx, counts = clsa.route(q_idx, K_idx, wl.k, n_ctx=nc)
+        out, _ = clsa.sparse_attn(q, Kc, Vc, idx, counts)
+        torch.cuda.synchronize()
+        for b in range(wl.B):  # the step's rows sit where it appended them
+            assert torch.equal(K_idx[b, n_ctx[b] - 1], new_kidx[t, b])
+            assert torch.equal(Kc[:, b, n_ctx[b] - 1], new_k[t, :, b])
+            assert torch.equal(Vc[:, b, n_ctx[b] - 1], new_v[t, :, b])
+        _check_route(idx, counts, q_idx, K_idx, n_ctx, -1, wl.k, wl.k)
+        rows = [(b, 0) for b in range(wl.B)]
+        o_lists = _oracle_lists(q_idx, K_idx, n_ctx, -1, wl.k, rows)
+        _, nsame = _attn_full_launch_vs_oracle(q, Kc, Vc, idx, out, o_lists,
+                                               list(range(wl.L)), wl.k)
+        assert nsame >= 2  # ties at the boundary are rare on these inputs
+    del K_idx, Kc, Vc
+    _free()
