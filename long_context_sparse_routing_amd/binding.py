@@ -98,6 +98,23 @@ def _check_dev(*ts):
                 raise ValueError("all tensors must be contiguous")
 
 
+def _need(cond: bool, msg: str, exc=ValueError):
+    if not cond:
+        raise exc(msg)
+
+
+def _check_shape(t: torch.Tensor, shape: tuple, name: str):
+    _need(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _check_i32(t: torch.Tensor | None, shape: tuple, name: str):
+    """int32 tensor of exactly `shape` (the library reads and writes it as such)."""
+    if t is None:
+        return
+    _need(t.dtype == torch.int32, f"{name} must be int32, got {t.dtype}", TypeError)
+    _check_shape(t, shape, name)
+
+
 def _workspace(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor:
     if ws is not None:
         if ws.numel() * ws.element_size() < nbytes:
@@ -144,14 +161,14 @@ def prepare_route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int,
                   ws: torch.Tensor | None = None, stream=None) -> Prepared:
     """clsa_route, marshalled: calling the result returns (idx, counts)."""
     lib = load_library()
-    B, M, d = q_idx.shape
-    n_cap = K_idx.shape[1]
+    B, M, d, n_cap = _route_shapes(q_idx, K_idx)
     cap = k if cap is None else cap
     dev = q_idx.device
     if idx is None:
         idx = torch.empty((B, M, cap), dtype=torch.int32, device=dev)
     if counts is None:
         counts = torch.empty((B, M), dtype=torch.int32, device=dev)
+    _check_route_io(B, M, cap, n_ctx, idx, counts)
     _check_dev(q_idx, K_idx, n_ctx, idx, counts)
     dt = _dt(q_idx)
     need = lib.clsa_route_workspace_size(B, M, d, n_cap, k, cap, dt)
@@ -160,6 +177,25 @@ def prepare_route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int,
             _ptr(counts), cap, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     return Prepared("clsa_route", lib.clsa_route, args, (idx, counts),
                     (q_idx, K_idx, n_ctx, idx, counts, ws))
+
+
+def _route_shapes(q_idx: torch.Tensor, K_idx: torch.Tensor):
+    """(B, M, d, n_cap) of a routing call; q_idx [B, M, d] and K_idx
+    [B, n_cap, d] must agree in B, d and dtype."""
+    _need(q_idx.dim() == 3, f"q_idx must be [B, M, d], got shape {tuple(q_idx.shape)}")
+    _need(K_idx.dim() == 3, f"K_idx must be [B, n_cap, d], got shape {tuple(K_idx.shape)}")
+    B, M, d = q_idx.shape
+    _need(K_idx.shape[0] == B and K_idx.shape[2] == d,
+          f"K_idx {tuple(K_idx.shape)} does not match q_idx {tuple(q_idx.shape)}")
+    _need(K_idx.dtype == q_idx.dtype, f"K_idx is {K_idx.dtype}, q_idx {q_idx.dtype}", TypeError)
+    _dt(q_idx)
+    return B, M, d, K_idx.shape[1]
+
+
+def _check_route_io(B, M, cap, n_ctx, idx, counts):
+    _check_i32(n_ctx, (B,), "n_ctx")
+    _check_i32(idx, (B, M, cap), "idx")
+    _check_i32(counts, (B, M), "counts")
 
 
 def route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int, n_ctx: torch.Tensor | None = None,
@@ -175,8 +211,7 @@ def prepare_route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch
                             ws: torch.Tensor | None = None, stream=None) -> Prepared:
     """clsa_route_threshold, marshalled: calling the result returns (idx, counts)."""
     lib = load_library()
-    B, M, d = q_idx.shape
-    n_cap = K_idx.shape[1]
+    B, M, d, n_cap = _route_shapes(q_idx, K_idx)
     dev = q_idx.device
     if idx is None:
         idx = torch.empty((B, M, cap), dtype=torch.int32, device=dev)
@@ -184,6 +219,8 @@ def prepare_route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch
         counts = torch.empty((B, M), dtype=torch.int32, device=dev)
     if tau.dtype != torch.float32:
         raise TypeError("tau must be float32")
+    _check_shape(tau, (B, M), "tau")
+    _check_route_io(B, M, cap, n_ctx, idx, counts)
     _check_dev(q_idx, K_idx, tau, n_ctx, idx, counts)
     dt = _dt(q_idx)
     need = lib.clsa_route_threshold_workspace_size(B, M, d, n_cap, cap, dt)
@@ -219,19 +256,32 @@ def prepare_sparse_attn(q, K, V, idx: torch.Tensor, counts: torch.Tensor, scale:
     L = len(ql)
     if not (len(Kl) == len(Vl) == L) or L < 1 or L > MAX_LAYERS:
         raise ValueError("q, K and V need the same number of layers (1..64)")
+    _need(ql[0].dim() == 4, f"q[l] must be [B, M, Hq, D], got shape {tuple(ql[0].shape)}")
+    _need(Kl[0].dim() == 4, f"K[l] must be [B, n_cap, Hkv, D], got shape {tuple(Kl[0].shape)}")
     B, M, Hq, D = ql[0].shape
     _, n_cap, Hkv, _ = Kl[0].shape
+    _need(idx.dim() == 3, f"idx must be [B, M, cap], got shape {tuple(idx.shape)}")
     cap = idx.shape[-1]
     dev = ql[0].device
     dt = _dt(ql[0])
     for t in ql + Kl + Vl:
         if t.dtype != ql[0].dtype:
             raise TypeError("q, K and V must share one dtype")
-    _check_dev(*ql, *Kl, *Vl, idx, counts)
+    for l in range(L):
+        _check_shape(ql[l], (B, M, Hq, D), f"q[{l}]")
+        _check_shape(Kl[l], (B, n_cap, Hkv, D), f"K[{l}]")
+        _check_shape(Vl[l], (B, n_cap, Hkv, D), f"V[{l}]")
+    _check_i32(idx, (B, M, cap), "idx")
+    _check_i32(counts, (B, M), "counts")
     if out is None:
         out = torch.empty((L, B, M, Hq, D), dtype=ql[0].dtype, device=dev)
     outl = _layers(out)
-    _check_dev(*outl)
+    _need(len(outl) == L, f"out has {len(outl)} layers, expected {L}")
+    for l in range(L):
+        _check_shape(outl[l], (B, M, Hq, D), f"out[{l}]")
+        _need(outl[l].dtype == ql[0].dtype, f"out[{l}] is {outl[l].dtype}, q {ql[0].dtype}",
+              TypeError)
+    _check_dev(*ql, *Kl, *Vl, idx, counts, *outl)
     lse = torch.empty((L, B, M, Hq), dtype=torch.float32, device=dev) if want_lse else None
     need = lib.clsa_sparse_attn_workspace_size(L, B, M, Hq, Hkv, D, cap, dt)
     ws = _workspace(need, dev, ws)
@@ -271,10 +321,24 @@ def prepare_kv_append(pos: torch.Tensor, src_idx=None, dst_idx=None, src_k=None,
     L = len(ks)
     if not (len(vs) == len(Kd) == len(Vd) == L):
         raise ValueError("src_k, K, src_v and V need the same number of layers")
+    _need(L > 0 or dst_idx is not None, "nothing to append")
+    _need((src_idx is None) == (dst_idx is None), "src_idx and dst_idx go together")
+    _check_i32(pos, (B,), "pos")
     ref = dst_idx if dst_idx is not None else Kd[0]
     n_cap = ref.shape[1]
     d = dst_idx.shape[2] if dst_idx is not None else 0
     Hkv, D = (Kd[0].shape[2], Kd[0].shape[3]) if L else (0, 0)
+    if dst_idx is not None:
+        _check_shape(dst_idx, (B, n_cap, d), "dst_idx")
+        _check_shape(src_idx, (B, d), "src_idx")
+    for l in range(L):
+        _check_shape(Kd[l], (B, n_cap, Hkv, D), f"K[{l}]")
+        _check_shape(Vd[l], (B, n_cap, Hkv, D), f"V[{l}]")
+        _check_shape(ks[l], (B, Hkv, D), f"src_k[{l}]")
+        _check_shape(vs[l], (B, Hkv, D), f"src_v[{l}]")
+    for t in [src_idx, dst_idx, *ks, *vs, *Kd, *Vd]:
+        if t is not None and t.dtype != ref.dtype:
+            raise TypeError("appended rows and caches must share one dtype")
     _check_dev(pos, src_idx, dst_idx, *ks, *vs, *Kd, *Vd)
     dt = _dt(ref)
     arr = ctypes.c_void_p * max(L, 1)

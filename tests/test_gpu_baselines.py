@@ -89,6 +89,7 @@ def test_per_layer_routing_pipeline():
     qn, Kn = f64(q_idx), f64(K_idx)
     scale = 1.0 / math.sqrt(D)
     G = Hq // Hkv
+    compared = 0
     for l in range(L):
         for b in range(B):
             r = l * B + b
@@ -97,9 +98,11 @@ def test_per_layer_routing_pipeline():
             o_idx = np.full(k, -1)
             o_idx[:len(sel)] = sel
             check_topk_row(gi[r, 0], int(gc[r, 0]), o_idx, len(sel), s, k)
-            # attention over the oracle's own list of this layer
-            Kl, Vl = f64(K[l, b][sel]), f64(V[l, b][sel])
+            # attention over this layer's own list as the GPU routed it
+            gsel = torch.from_numpy(gi[r, 0, : int(gc[r, 0])].astype(np.int64))
+            Kl, Vl = f64(K[l, b][gsel]), f64(V[l, b][gsel])
             for h in range(Hq):
                 o_ref, _ = O.attend_head(f64(q[l, b, 0, h]), Kl[:, h // G], Vl[:, h // G], scale)
-                if np.array_equal(np.sort(gi[r, 0, :k]), sel):
-                    assert np.max(np.abs(f64(outs[l][0, b, 0, h]) - o_ref)) <= 2e-2
+                assert np.max(np.abs(f64(outs[l][0, b, 0, h]) - o_ref)) <= 2e-2
+                compared += 1
+    assert compared == L * B * Hq
