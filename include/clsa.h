@@ -24,7 +24,9 @@
  *    workspace `ws` of at least the size returned by the matching
  *    *_workspace_size function (same shape arguments).  A size of 0 means
  *    either that the call needs no workspace (ws may then be NULL) or that
- *    the call would reject the shapes.
+ *    the call would reject the shapes.  The one exception is
+ *    clsa_route_static, whose scratch is a fixed device array of the
+ *    library (see there).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues work on it and returns without synchronizing.  Calls that share
  *    one workspace must be ordered (same stream, or synchronized).
@@ -66,7 +68,9 @@ typedef enum clsa_status {
   CLSA_ERR_INVALID = -1,           /* null pointer, bad shape or size */
   CLSA_ERR_WORKSPACE = -2,         /* ws too small (or NULL with a nonzero need) */
   CLSA_ERR_UNSUPPORTED_DTYPE = -3, /* dtype not CLSA_F32 / CLSA_BF16 */
-  CLSA_ERR_HIP = -4                /* a kernel launch failed */
+  CLSA_ERR_HIP = -4,               /* a kernel launch failed */
+  CLSA_ERR_SCRATCH_LIMIT = -5      /* clsa_route_static: the shapes need more
+                                      than CLSA_STATIC_SCRATCH_BYTES */
 } clsa_status;
 
 /* Library version (CLSA_VERSION of the build). */
@@ -122,6 +126,35 @@ size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, int k, int 
 int clsa_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
                const int32_t* n_ctx, int64_t q_pos0, int k, clsa_dtype dt, int32_t* idx,
                int32_t* counts, int cap, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * clsa_route_static - clsa_route for callers that cannot allocate.
+ * For callers that may not call hipMalloc or any allocating routine
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and results as clsa_route,
+ * with the workspace taken from a fixed array of CLSA_STATIC_SCRATCH_BYTES
+ * in device memory that the library holds on every GPU it runs on, until
+ * the process ends.  The caller still passes the inputs and outputs.
+ *
+ * Arguments are those of clsa_route without ws / ws_bytes.  The call runs
+ * on the calling thread's current device, which must be the device of
+ * `stream`.  It allocates nothing (the array's address is looked up once per
+ * device, on the first call there).
+ * Shapes whose clsa_route_workspace_size exceeds CLSA_STATIC_SCRATCH_BYTES
+ * are rejected with CLSA_ERR_SCRATCH_LIMIT before anything is enqueued:
+ * with bf16 keys and k <= 2048, up to 146 decode rows (M = 1) at any context
+ * length up to 512K fit.
+ * Every call on one GPU uses that GPU's one array, which keeps the previous
+ * call's contents (the kernels clear what they need zeroed): calls that
+ * overlap on one GPU (different streams, or different host threads without
+ * ordering) race and give undefined results.  Order them on one stream.
+ * Errors: as clsa_route, plus CLSA_ERR_SCRATCH_LIMIT, and CLSA_ERR_HIP when
+ * the current device cannot be queried.
+ */
+#define CLSA_STATIC_SCRATCH_BYTES (8u << 20)
+int clsa_route_static(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                      const int32_t* n_ctx, int64_t q_pos0, int k, clsa_dtype dt, int32_t* idx,
+                      int32_t* counts, int cap, void* stream);
 
 /*
  * clsa_route_threshold - half-space selection with no false negatives.

@@ -10,9 +10,11 @@ from .binding import (  # noqa: F401
     load_library,
     prepare_kv_append,
     prepare_route,
+    prepare_route_static,
     prepare_route_threshold,
     prepare_sparse_attn,
     route,
+    route_static,
     route_threshold,
     route_threshold_workspace_size,
     route_workspace_size,

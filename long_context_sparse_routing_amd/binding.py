@@ -20,7 +20,8 @@ CLSA_BF16 = 1
 MAX_LAYERS = 64
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "workspace too small",
-           -3: "unsupported dtype", -4: "HIP launch failure"}
+           -3: "unsupported dtype", -4: "HIP launch failure",
+           -5: "shapes exceed the static scratch array"}
 
 
 class ClsaError(RuntimeError):
@@ -54,6 +55,9 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.clsa_route.restype = i32
     lib.clsa_route.argtypes = [vp, vp, i32, i32, i32, i64, vp, i64, i32, i32, vp, vp, i32, vp,
                                sz, vp]
+    lib.clsa_route_static.restype = i32
+    lib.clsa_route_static.argtypes = [vp, vp, i32, i32, i32, i64, vp, i64, i32, i32, vp, vp, i32,
+                                      vp]
     lib.clsa_route_threshold_workspace_size.restype = sz
     lib.clsa_route_threshold_workspace_size.argtypes = [i32, i32, i32, i64, i32, i32]
     lib.clsa_route_threshold.restype = i32
@@ -203,6 +207,39 @@ def route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int, n_ctx: torch.Tensor 
           counts: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
     """clsa_route: q_idx [B, M, d], K_idx [B, n_cap, d] -> (idx [B, M, cap], counts [B, M])."""
     return prepare_route(q_idx, K_idx, k, n_ctx, q_pos0, cap, idx, counts, ws, stream)()
+
+
+def prepare_route_static(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int,
+                         n_ctx: torch.Tensor | None = None, q_pos0: int = -1,
+                         cap: int | None = None, idx: torch.Tensor | None = None,
+                         counts: torch.Tensor | None = None, stream=None) -> Prepared:
+    """clsa_route_static, marshalled: the routing of clsa_route on the
+    library's fixed device scratch array, so the call itself allocates
+    nothing (pass idx and counts to keep the binding from allocating them).
+    Calls on one GPU share that array: order them on one stream."""
+    lib = load_library()
+    B, M, d, n_cap = _route_shapes(q_idx, K_idx)
+    cap = k if cap is None else cap
+    dev = q_idx.device
+    if idx is None:
+        idx = torch.empty((B, M, cap), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((B, M), dtype=torch.int32, device=dev)
+    _check_route_io(B, M, cap, n_ctx, idx, counts)
+    _check_dev(q_idx, K_idx, n_ctx, idx, counts)
+    dt = _dt(q_idx)
+    args = (_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0, k, dt, _ptr(idx),
+            _ptr(counts), cap, _stream(stream))
+    return Prepared("clsa_route_static", lib.clsa_route_static, args, (idx, counts),
+                    (q_idx, K_idx, n_ctx, idx, counts))
+
+
+def route_static(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int,
+                 n_ctx: torch.Tensor | None = None, q_pos0: int = -1, cap: int | None = None,
+                 idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                 stream=None):
+    """clsa_route_static: as route(), with no workspace argument."""
+    return prepare_route_static(q_idx, K_idx, k, n_ctx, q_pos0, cap, idx, counts, stream)()
 
 
 def prepare_route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor,

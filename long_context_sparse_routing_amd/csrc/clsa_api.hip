@@ -99,6 +99,7 @@ extern "C" const char* clsa_status_string(int status) {
     case CLSA_ERR_WORKSPACE: return "workspace too small";
     case CLSA_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
     case CLSA_ERR_HIP: return "HIP launch failure";
+    case CLSA_ERR_SCRATCH_LIMIT: return "shapes exceed the static scratch array";
     default: return "unknown status";
   }
 }

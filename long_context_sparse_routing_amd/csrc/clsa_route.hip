@@ -41,6 +41,8 @@
 // candidate list;
 // block_select (clsa_prefill.hip) takes the exact top-k of those candidates.
 // Scores are the same in both paths.
+#include <mutex>
+
 #include "clsa_common.h"
 
 namespace clsa {
@@ -795,14 +797,26 @@ extern "C" size_t clsa_route_workspace_size(int B, int M, int d, int64_t n_cap, 
   return make_layout((int64_t)B * M, n_cap, true).total;
 }
 
-extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, int d,
-                          int64_t n_cap, const int32_t* n_ctx, int64_t q_pos0, int k,
-                          clsa_dtype dt, int32_t* idx, int32_t* counts, int cap, void* ws,
-                          size_t ws_bytes, void* stream) {
+namespace clsa {
+namespace {
+// Argument checks of clsa_route that need no workspace: the status to
+// return, CLSA_OK when the call may proceed.
+int route_args_status(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                      int k, clsa_dtype dt, const int32_t* idx, const int32_t* counts, int cap) {
   if (dt != CLSA_F32 && dt != CLSA_BF16) return CLSA_ERR_UNSUPPORTED_DTYPE;
   if (!q_idx || !K_idx || !idx || !counts) return CLSA_ERR_INVALID;
   if (!shape_ok(B, M, d, n_cap, cap) || k < 1 || cap < k) return CLSA_ERR_INVALID;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return CLSA_OK;
+}
+
+// clsa_route on a workspace `ws` of `ws_bytes`: picks the block, filter or
+// exhaustive path and enqueues its kernels.  Every path clears what it
+// needs zeroed with kernels, so the workspace may hold anything on entry.
+int route_call(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
+               const int32_t* n_ctx, int64_t q_pos0, int k, clsa_dtype dt, int32_t* idx,
+               int32_t* counts, int cap, void* ws, size_t ws_bytes, hipStream_t s) {
+  const int st = route_args_status(q_idx, K_idx, B, M, d, n_cap, k, dt, idx, counts, cap);
+  if (st != CLSA_OK) return st;
   if (block_route_applies(M, d, n_cap, k, dt)) {
     if (!ws || ws_bytes < block_route_workspace(B, M, d, n_cap)) return CLSA_ERR_WORKSPACE;
     return block_route(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, ws, s);
@@ -846,6 +860,62 @@ extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, in
   hipLaunchKernelGGL(route_select, dim3((unsigned)R), dim3(kNT), 0, s, a);
   hipLaunchKernelGGL(route_compact<true>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
+}
+}  // namespace
+}  // namespace clsa
+
+extern "C" int clsa_route(const void* q_idx, const void* K_idx, int B, int M, int d,
+                          int64_t n_cap, const int32_t* n_ctx, int64_t q_pos0, int k,
+                          clsa_dtype dt, int32_t* idx, int32_t* counts, int cap, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return route_call(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, dt, idx, counts, cap, ws,
+                    ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+// ------------------------------------------------------- no-allocation routing
+// clsa_route_static runs clsa_route's kernels on a fixed device array in
+// place of a caller workspace.  `scratch` is a host-side stand-in for that
+// array; host code only ever uses the address hipGetSymbolAddress returns
+// for it on the current device (each GPU holds its own copy).
+static __device__ __align__(256) unsigned char scratch[CLSA_STATIC_SCRATCH_BYTES];
+
+namespace clsa {
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the calling thread's current device,
+// looked up once per device and kept.
+int static_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CLSA_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return CLSA_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return CLSA_OK;
+}
+}  // namespace
+}  // namespace clsa
+
+extern "C" int clsa_route_static(const void* q_idx, const void* K_idx, int B, int M, int d,
+                                 int64_t n_cap, const int32_t* n_ctx, int64_t q_pos0, int k,
+                                 clsa_dtype dt, int32_t* idx, int32_t* counts, int cap,
+                                 void* stream) {
+  const int st = route_args_status(q_idx, K_idx, B, M, d, n_cap, k, dt, idx, counts, cap);
+  if (st != CLSA_OK) return st;
+  if (clsa_route_workspace_size(B, M, d, n_cap, k, cap, dt) > (size_t)CLSA_STATIC_SCRATCH_BYTES)
+    return CLSA_ERR_SCRATCH_LIMIT;
+  void* ptr = nullptr;
+  const int sst = static_scratch(&ptr);
+  if (sst != CLSA_OK) return sst;
+  return route_call(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, dt, idx, counts, cap, ptr,
+                    (size_t)CLSA_STATIC_SCRATCH_BYTES, static_cast<hipStream_t>(stream));
 }
 
 extern "C" size_t clsa_route_threshold_workspace_size(int B, int M, int d, int64_t n_cap, int cap,

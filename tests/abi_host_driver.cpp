@@ -121,6 +121,17 @@ void route_rejects() {
                               c.ws_bytes, nullptr);
     EXPECT(st == c.want);
   }
+  // the allocation-free variant validates the same way, then refuses shapes
+  // that need more than its fixed array, all before any GPU call
+  EXPECT(clsa_route_static(nullptr, kFake, 1, 1, 64, 4096, nullptr, -1, 256, CLSA_BF16, fi, fi,
+                           256, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_route_static(kFake, kFake, 1, 1, 64, 4096, nullptr, -1, 256,
+                           static_cast<clsa_dtype>(5), fi, fi, 256, nullptr) ==
+         CLSA_ERR_UNSUPPORTED_DTYPE);
+  EXPECT(clsa_route_static(kFake, kFake, 147, 1, 64, 131072, nullptr, -1, 2048, CLSA_BF16, fi, fi,
+                           2048, nullptr) == CLSA_ERR_SCRATCH_LIMIT);
+  EXPECT(clsa_route_static(kFake, kFake, 1, 4096, 64, 131072, nullptr, -1, 2048, CLSA_BF16, fi,
+                           fi, 2048, nullptr) == CLSA_ERR_SCRATCH_LIMIT);
   const float* ft = static_cast<const float*>(kFake);
   EXPECT(clsa_route_threshold(kFake, kFake, 1, 1, 64, 4096, nullptr, -1, nullptr, CLSA_BF16, fi,
                               fi, 64, kFake, big, nullptr) == CLSA_ERR_INVALID);

@@ -163,3 +163,31 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def _route_static(lib, q=FAKE, K=FAKE, B=1, M=1, d=64, n_cap=4096, k=256, dt=BF16, idx=FAKE,
+                  counts=FAKE, cap=256):
+    return lib.clsa_route_static(q, K, B, M, d, n_cap, NULL, -1, k, dt, idx, counts, cap, NULL)
+
+
+SCRATCH_LIMIT = -5
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INVALID), (dict(idx=NULL), INVALID), (dict(counts=NULL), INVALID),
+    (dict(d=48), INVALID), (dict(k=0), INVALID), (dict(cap=100), INVALID),
+    (dict(dt=7), DTYPE), (dict(B=70000), INVALID),
+    # shapes whose workspace passes the fixed array: refused before any GPU call
+    (dict(B=147, n_cap=131072, k=2048, cap=2048), SCRATCH_LIMIT),
+    (dict(B=1, M=4096, n_cap=131072, k=2048, cap=2048), SCRATCH_LIMIT),
+    (dict(B=8, n_cap=131072, k=2048, cap=2048, dt=F32), SCRATCH_LIMIT),
+])
+def test_route_static_rejects(lib, kw, want):
+    assert _route_static(lib, **kw) == want
+
+
+def test_route_static_limit_is_the_workspace_size(lib):
+    limit = 8 << 20  # CLSA_STATIC_SCRATCH_BYTES
+    assert lib.clsa_route_workspace_size(146, 1, 64, 131072, 2048, 2048, BF16) <= limit
+    assert lib.clsa_route_workspace_size(147, 1, 64, 131072, 2048, 2048, BF16) > limit
+    assert lib.clsa_status_string(SCRATCH_LIMIT) == b"shapes exceed the static scratch array"

@@ -23,7 +23,7 @@ def _route_args():
     return torch.zeros((2, 1, 64), dtype=bf), torch.zeros((2, 100, 64), dtype=bf)
 
 
-@pytest.mark.parametrize("fn", ["prepare_route"])
+@pytest.mark.parametrize("fn", ["prepare_route", "prepare_route_static"])
 @pytest.mark.parametrize("bad,exc,msg", [
     (dict(K_idx=torch.zeros((3, 100, 64), dtype=bf)), ValueError, "does not match"),
     (dict(K_idx=torch.zeros((2, 100, 32), dtype=bf)), ValueError, "does not match"),
