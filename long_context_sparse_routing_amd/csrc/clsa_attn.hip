@@ -197,13 +197,13 @@ CLSA_DEV u32x4_t load_row16(const uint16_t* p) {
   else return *reinterpret_cast<const u32x4_t*>(p);
 }
 
-template <int G, int D, bool NT>
+template <int G, int D, bool NT, int AB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 4 : (G <= 8 ? 3 : 2), 8)))
 void attn_bf16(AttnArgs a) {
   constexpr int kLPT = D / 8;      // lanes per token row (8 dims each)
   constexpr int kTPW = 64 / kLPT;  // token rows per wave load
   constexpr int kTS = ts_max(G);
-  constexpr int kAB = 2;           // K rows in flight per lane
+  constexpr int kAB = AB;          // K rows in flight per lane
   constexpr int kVB = 4;           // V rows in flight per lane
   constexpr int kNR = G / kLPT > 0 ? G / kLPT : 1;  // sums per lane after the reduce
   constexpr int kShare = kLPT / (G < kLPT ? G : kLPT);  // lanes holding the same sums
@@ -544,16 +544,23 @@ Plan make_plan(int L, int B, int M, int Hq, int Hkv, int D, int cap, clsa_dtype 
   return p;
 }
 
-template <int G, bool NT>
-void launch_fast_gn(int D, dim3 grid, dim3 block, hipStream_t s, const AttnArgs& a) {
-  if (D == 128) hipLaunchKernelGGL((attn_bf16<G, 128, NT>), grid, block, 0, s, a);
-  else if (D == 64) hipLaunchKernelGGL((attn_bf16<G, 64, NT>), grid, block, 0, s, a);
-  else if constexpr (G <= 8) hipLaunchKernelGGL((attn_bf16<G, 256, NT>), grid, block, 0, s, a);
+template <int G, bool NT, int AB>
+void launch_fast_gna(int D, dim3 grid, dim3 block, hipStream_t s, const AttnArgs& a) {
+  if (D == 128) hipLaunchKernelGGL((attn_bf16<G, 128, NT, AB>), grid, block, 0, s, a);
+  else if (D == 64) hipLaunchKernelGGL((attn_bf16<G, 64, NT, AB>), grid, block, 0, s, a);
+  else if constexpr (G <= 8) hipLaunchKernelGGL((attn_bf16<G, 256, NT, AB>), grid, block, 0, s, a);
 }
+// K rows in flight per lane: 4 where a workgroup's split is short (its
+// few load rounds are latency-bound: 16 single-layer decode launches 367 ->
+// 345 us) or rows share positions (cached loads); 2 for long streaming
+// splits, whose loads already keep HBM busy (the 16-layer decode launch is
+// 1 % slower with 4).
 template <int G>
-void launch_fast_g(int D, bool nt, dim3 grid, dim3 block, hipStream_t s, const AttnArgs& a) {
-  if (nt) launch_fast_gn<G, true>(D, grid, block, s, a);
-  else launch_fast_gn<G, false>(D, grid, block, s, a);
+void launch_fast_g(int D, bool nt, bool short_split, dim3 grid, dim3 block, hipStream_t s,
+                   const AttnArgs& a) {
+  if (nt && !short_split) launch_fast_gna<G, true, 2>(D, grid, block, s, a);
+  else if (nt) launch_fast_gna<G, true, 4>(D, grid, block, s, a);
+  else launch_fast_gna<G, false, 4>(D, grid, block, s, a);
 }
 
 // Streaming loads unless a routed K/V row is expected to be read at least
@@ -622,12 +629,13 @@ extern "C" int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D,
     const dim3 block(64 * kWaves);
     const dim3 mgrid((unsigned)(p.S * Hkv), (unsigned)R, (unsigned)L);
     const bool nt = attn_streaming(M, cap, n_cap);
+    const bool sh = p.S > 1;
     switch (Hq / Hkv) {
-      case 1: launch_fast_g<1>(D, nt, mgrid, block, s, a); break;
-      case 2: launch_fast_g<2>(D, nt, mgrid, block, s, a); break;
-      case 4: launch_fast_g<4>(D, nt, mgrid, block, s, a); break;
-      case 8: launch_fast_g<8>(D, nt, mgrid, block, s, a); break;
-      default: launch_fast_g<16>(D, nt, mgrid, block, s, a); break;
+      case 1: launch_fast_g<1>(D, nt, sh, mgrid, block, s, a); break;
+      case 2: launch_fast_g<2>(D, nt, sh, mgrid, block, s, a); break;
+      case 4: launch_fast_g<4>(D, nt, sh, mgrid, block, s, a); break;
+      case 8: launch_fast_g<8>(D, nt, sh, mgrid, block, s, a); break;
+      default: launch_fast_g<16>(D, nt, sh, mgrid, block, s, a); break;
     }
   } else if (dt == CLSA_BF16) {
     hipLaunchKernelGGL(attn_generic<uint16_t>, grid, dim3(256), 0, s, a);
