@@ -479,6 +479,66 @@ def threshold_step(dev, reps, cpu_budget=0.0):
             "step_hbm_frac": step_bytes / (step_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
 
 
+def louver_leg(dev, reps):
+    """Threshold selection through the Louver index (Louver summary, sections
+    on the index and its query algorithms) against the exhaustive scan of
+    clsa_route_threshold, on the threshold workload's shapes (16 x 128K
+    keys, d_idx 128, 256 .. 8192 keys per row): once on its Gaussian keys and
+    once on clustered keys (64 centers per sequence, sigma 0.05), where an
+    index can prune.  Reports the build, each query's time, the share of
+    keys scored exactly and the bytes each query reads."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+    wl = gen.WORKLOADS["threshold_128k_b16"]
+    cap, r = 8192, 64
+    out = {"workload": wl.name, "sequences": wl.B, "n": wl.n_ctx, "d_idx": wl.d, "r": r}
+    for name, clusters in (("gaussian_keys", 0), ("clustered_keys", 64)):
+        K_cpu, q_cpu, tau = gen.gen_threshold_inputs(wl, lambda qq, KK: KK @ qq,
+                                                     clusters=clusters)
+        K, q, tau_d = K_cpu.to(dev), q_cpu.to(dev), tau.to(dev)
+        ref = clsa.prepare_route_threshold(q, K, tau_d, cap)
+        ref_idx, ref_cnt = [t.clone() for t in ref()]
+        scan_bytes = wl.B * wl.n_ctx * wl.d * 2
+        exh_ms = _event_ms(ref, reps)
+        leg = {"exhaustive": {"ms_per_call": exh_ms, "bytes": scan_bytes,
+                              "GBs": scan_bytes / (exh_ms * 1e-3) / 1e9}}
+        for S, mode in ((1, 1), (4, 1), (4, 2)):
+            ix = clsa.LouverIndex(wl.B, wl.d, wl.n_ctx, S=S, r=r, device=dev)
+            ix.build(K, wl.n_ctx)  # first build: kernels load
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ix2 = clsa.LouverIndex(wl.B, wl.d, wl.n_ctx, S=S, r=r, device=dev)
+            e0.record()
+            ix2.build(K, wl.n_ctx)
+            e1.record()
+            torch.cuda.synchronize()
+            build_ms = e0.elapsed_time(e1)
+            chk = torch.zeros(wl.B, dtype=torch.int32, device=dev)
+            qc = ix.prepare_query(q, K, tau_d, cap, mode=mode, checked=chk)
+            idx, cnt, _ = qc()
+            torch.cuda.synchronize()
+            same = torch.equal(idx, ref_idx) and torch.equal(cnt, ref_cnt)
+            if not same:
+                raise RuntimeError(f"Louver query (S={S}, mode={mode}) differs from the scan")
+            ms = _event_ms(qc, reps)
+            checked = int(chk.sum())
+            C = 1 << max(0, math.ceil(math.log2(wl.n_ctx / r)))
+            q_bytes = (wl.B * S * C * (wl.d // S * 2 + 4)  # centers and radii
+                       + checked * (wl.d * 2 + 4)            # keys scored and their slots
+                       + (wl.B * S * wl.n_ctx * 2 if S > 1 and mode == 1 else 0))  # cluster ids
+            leg[f"S{S}_query{mode}"] = {
+                "build_ms": build_ms, "ms_per_call": ms, "speedup_vs_exhaustive": exh_ms / ms,
+                "keys_checked_frac": checked / (wl.B * wl.n_ctx), "bytes": q_bytes,
+                "bytes_vs_scan": q_bytes / scan_bytes, "GBs": q_bytes / (ms * 1e-3) / 1e9,
+                "matches_exhaustive": same}
+            del ix, ix2, qc
+        out[name] = leg
+        del K, ref
+        torch.cuda.empty_cache()
+    return out
+
+
 def tiny_fp32_step(dev, reps, cpu_budget=0.0):
     """The smallest configuration: one fp32 sequence at 4K context, d_idx 32,
     one layer with one head of dim 64, k = 256 -- a routing call plus an
@@ -788,6 +848,7 @@ def main():
         res["threshold_128k_b16"] = threshold_step(dev, 5, cb)
         res["decode_32k"] = decode_32k_step(dev, 64, cb)
         res["tiny_fp32_4k"] = tiny_fp32_step(dev, 200, min(1.0, cb))
+        res["louver"] = louver_leg(dev, 5)
     if args.prefill_calls > 0:
         res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget),
                                                  bool(args.prefill_attention))

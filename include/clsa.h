@@ -208,6 +208,62 @@ int clsa_sparse_attn(int L, int B, int M, int Hq, int Hkv, int D, const void* co
                      void* stream);
 
 /*
+ * Louver index - threshold selection that checks only the keys of clusters
+ * whose bounding ball reaches the query's half-space.
+ * (Louver summary, gist.science, section "2. Louver インデックス": the key
+ * space is cut into S contiguous subspaces; in each, a balanced PCA tree
+ * groups the keys into clusters of at most r keys, each wrapped in a
+ * bounding ball; a query prunes the clusters whose ball misses the
+ * half-space and checks the others' keys exactly; keys added while decoding
+ * wait in a buffer and are clustered into the index when it fills.
+ * Section "クエリアルゴリズム": Query 1 (mode 1) prunes every subspace with
+ * its own threshold; Query 2 (mode 2) is the threshold algorithm: clusters
+ * scanned in descending bound until the bounds of the next depth sum below
+ * tau.  Both have no false negatives.)
+ *
+ * The index of B sequences covers key positions [0, n_max) of K_idx
+ * [B][n_cap][d] (bf16, d = 32, 64 or 128) in segments: segment k is one
+ * tree over positions [seg_bounds[k], seg_bounds[k+1]) of every sequence,
+ * with seg_bounds[0] = 0, strictly increasing, at most 16 segments, at most
+ * 8192 clusters per segment.  S is 1, 2 or 4 (d / S a multiple of 8);
+ * 8 <= r <= 256; n_max <= 2^24.
+ *
+ *   index   caller-owned device buffer of clsa_louver_index_bytes(...).
+ *   clsa_louver_build builds segment nseg - 1 of an index whose segments
+ *           0 .. nseg - 2 were built by earlier calls (so clustering the
+ *           buffer of appended keys is one more call; nothing is rebuilt).
+ *           seg_bounds is a HOST array of nseg + 1 entries, last <= n_cap;
+ *           every sequence must hold valid keys up to it.  ws: device
+ *           workspace of clsa_louver_build_workspace_size(...).
+ *   clsa_louver_query selects, for each sequence b (one query row each:
+ *           q_idx [B][d], tau [B] float DEVICE, n_ctx [B] int32 DEVICE or
+ *           NULL), every visible position j (j < n_ctx[b]) with
+ *           q_idx[b] . K_idx[b][j] >= tau[b] -- fp32 sums of exact products,
+ *           compared in fp32 as in clsa_route_threshold, so the results are
+ *           the same.  Positions past seg_bounds[nseg] are checked exactly
+ *           (the buffer).  Outputs as clsa_route_threshold (M = 1): idx
+ *           [B][cap] ascending then -1, counts [B] the true set size.
+ *           checked [B] (device, may be NULL) receives the number of keys
+ *           whose exact score the query computed.  The index must have been
+ *           built with the same B, d, S, r, n_max and segments.
+ * Errors: CLSA_ERR_INVALID (null pointer, shapes, segments, mode not 1/2,
+ * index_bytes too small), CLSA_ERR_UNSUPPORTED_DTYPE (not CLSA_BF16),
+ * CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.
+ */
+size_t clsa_louver_index_bytes(int B, int d, int64_t n_max, int S, int r);
+size_t clsa_louver_build_workspace_size(int B, int d, int64_t n_max, int S, int r);
+int clsa_louver_build(const void* K_idx, int B, int d, int64_t n_cap, clsa_dtype dt, int S, int r,
+                      int64_t n_max, int nseg, const int64_t* seg_bounds, void* index,
+                      size_t index_bytes, void* ws, size_t ws_bytes, void* stream);
+size_t clsa_louver_query_workspace_size(int B, int d, int64_t n_cap, int S, int r, int64_t n_max,
+                                        int nseg, const int64_t* seg_bounds);
+int clsa_louver_query(const void* q_idx, const void* K_idx, int B, int d, int64_t n_cap,
+                      const int32_t* n_ctx, const float* tau, clsa_dtype dt, int S, int r,
+                      int64_t n_max, int nseg, const int64_t* seg_bounds, const void* index,
+                      int mode, int32_t* idx, int32_t* counts, int cap, uint32_t* checked,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/*
  * clsa_kv_append - write one new token's rows into preallocated caches.
  * (CLSA explainer, section "CLSAの仕組み": the self-decoder writes the KV
  * cache that every cross-decoder layer then reads.)  This is that per-step

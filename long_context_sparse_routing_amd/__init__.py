@@ -5,6 +5,7 @@ The compute path is libclsa.so (hand-written HIP for gfx950) behind a C ABI
 """
 from .binding import (  # noqa: F401
     ClsaError,
+    LouverIndex,
     Prepared,
     kv_append,
     load_library,

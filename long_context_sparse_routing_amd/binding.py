@@ -68,6 +68,18 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.clsa_sparse_attn.restype = i32
     lib.clsa_sparse_attn.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp, vp, i64, vp, vp, i32,
                                      ctypes.c_float, i32, vp, vp, vp, sz, vp]
+    lib.clsa_louver_index_bytes.restype = sz
+    lib.clsa_louver_index_bytes.argtypes = [i32, i32, i64, i32, i32]
+    lib.clsa_louver_build_workspace_size.restype = sz
+    lib.clsa_louver_build_workspace_size.argtypes = [i32, i32, i64, i32, i32]
+    lib.clsa_louver_build.restype = i32
+    lib.clsa_louver_build.argtypes = [vp, i32, i32, i64, i32, i32, i32, i64, i32, vp, vp, sz, vp,
+                                      sz, vp]
+    lib.clsa_louver_query_workspace_size.restype = sz
+    lib.clsa_louver_query_workspace_size.argtypes = [i32, i32, i64, i32, i32, i64, i32, vp]
+    lib.clsa_louver_query.restype = i32
+    lib.clsa_louver_query.argtypes = [vp, vp, i32, i32, i64, vp, vp, i32, i32, i32, i64, i32, vp,
+                                      vp, i32, vp, vp, i32, vp, vp, sz, vp]
     lib.clsa_kv_append.restype = i32
     lib.clsa_kv_append.argtypes = [i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32,
                                    vp]
@@ -389,3 +401,90 @@ def prepare_kv_append(pos: torch.Tensor, src_idx=None, dst_idx=None, src_k=None,
 def kv_append(pos, src_idx=None, dst_idx=None, src_k=None, K=None, src_v=None, V=None,
               stream=None):
     prepare_kv_append(pos, src_idx, dst_idx, src_k, K, src_v, V, stream)()
+
+
+class LouverIndex:
+    """A Louver index (clsa_louver_build / clsa_louver_query) over the routing
+    keys of B sequences: the device buffer and the host table of segment
+    bounds that every call passes.  build(K_idx, end) clusters positions
+    [last end, end) into a new segment; query(...) is the threshold
+    selection of clsa_route_threshold through the index."""
+
+    def __init__(self, B: int, d: int, n_max: int, S: int = 1, r: int = 64, device="cuda"):
+        lib = load_library()
+        nbytes = lib.clsa_louver_index_bytes(B, d, n_max, S, r)
+        if nbytes == 0:
+            raise ValueError(f"unsupported Louver index shape B={B} d={d} n_max={n_max} S={S} r={r}")
+        self.B, self.d, self.n_max, self.S, self.r = B, d, n_max, S, r
+        # zeroed once, so that two indexes built from the same keys compare
+        # equal byte for byte (the build writes every part a query reads)
+        self.buf = torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        self.bounds: list[int] = [0]
+
+    @property
+    def indexed(self) -> int:
+        """Positions covered by the index; later ones are the buffer."""
+        return self.bounds[-1]
+
+    def _bounds(self, extra=None):
+        b = self.bounds + ([extra] if extra is not None else [])
+        return (ctypes.c_int64 * len(b))(*b), len(b) - 1
+
+    def build(self, K_idx: torch.Tensor, end: int, ws: torch.Tensor | None = None, stream=None):
+        lib = load_library()
+        _need(K_idx.dim() == 3 and K_idx.shape[0] == self.B and K_idx.shape[2] == self.d,
+              f"K_idx {tuple(K_idx.shape)} does not match the index (B={self.B}, d={self.d})")
+        _need(K_idx.dtype == torch.bfloat16, "the Louver index takes bfloat16 keys", TypeError)
+        _need(self.indexed < end <= min(self.n_max, K_idx.shape[1]),
+              f"segment end {end} must lie in ({self.indexed}, {min(self.n_max, K_idx.shape[1])}]")
+        _check_dev(K_idx)
+        arr, nseg = self._bounds(end)
+        need = lib.clsa_louver_build_workspace_size(self.B, self.d, self.n_max, self.S, self.r)
+        ws = _workspace(need, K_idx.device, ws)
+        st = lib.clsa_louver_build(_ptr(K_idx), self.B, self.d, K_idx.shape[1], CLSA_BF16, self.S,
+                                   self.r, self.n_max, nseg, arr, _ptr(self.buf),
+                                   self.buf.numel(), _ptr(ws), ws.numel(), _stream(stream))
+        if st != 0:
+            raise ClsaError("clsa_louver_build", st)
+        self.bounds.append(int(end))
+        self._keep = ws  # the build runs asynchronously on the stream
+
+    def prepare_query(self, q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch.Tensor,
+                      cap: int, mode: int = 1, n_ctx: torch.Tensor | None = None,
+                      idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                      checked: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                      stream=None) -> Prepared:
+        """clsa_louver_query, marshalled: calling the result returns
+        (idx [B, 1, cap], true counts [B, 1], checked [B] or None)."""
+        lib = load_library()
+        B, M, d, n_cap = _route_shapes(q_idx, K_idx)
+        _need(B == self.B and d == self.d and M == 1,
+              f"q_idx {tuple(q_idx.shape)} does not match the index (B={self.B}, d={self.d}, M=1)")
+        _need(self.indexed > 0, "the index has no segment yet")
+        if tau.dtype != torch.float32:
+            raise TypeError("tau must be float32")
+        _check_shape(tau, (B, 1), "tau")
+        dev = q_idx.device
+        if idx is None:
+            idx = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
+        if counts is None:
+            counts = torch.empty((B, 1), dtype=torch.int32, device=dev)
+        _check_route_io(B, 1, cap, n_ctx, idx, counts)
+        if checked is not None:
+            _check_shape(checked, (B,), "checked")
+            _need(checked.dtype == torch.int32, "checked must be int32", TypeError)
+        _check_dev(q_idx, K_idx, tau, n_ctx, idx, counts, checked)
+        arr, nseg = self._bounds()
+        need = lib.clsa_louver_query_workspace_size(B, d, n_cap, self.S, self.r, self.n_max, nseg,
+                                                    arr)
+        ws = _workspace(need, dev, ws)
+        args = (_ptr(q_idx), _ptr(K_idx), B, d, n_cap, _ptr(n_ctx), _ptr(tau), _dt(q_idx), self.S,
+                self.r, self.n_max, nseg, arr, _ptr(self.buf), mode, _ptr(idx), _ptr(counts), cap,
+                _ptr(checked), _ptr(ws), ws.numel(), _stream(stream))
+        return Prepared("clsa_louver_query", lib.clsa_louver_query, args, (idx, counts, checked),
+                        (q_idx, K_idx, tau, n_ctx, idx, counts, checked, ws, arr, self.buf))
+
+    def query(self, q_idx, K_idx, tau, cap, mode=1, n_ctx=None, idx=None, counts=None,
+              checked=None, ws=None, stream=None):
+        return self.prepare_query(q_idx, K_idx, tau, cap, mode, n_ctx, idx, counts, checked, ws,
+                                  stream)()

@@ -215,13 +215,19 @@ def threshold_counts(B: int, lo: int = 256, hi: int = 8192):
 
 
 def gen_threshold_inputs(wl: Workload, score_fn, device="cpu", seed: int | None = None,
-                         margin: float = 1e-4, counts=None, max_rounds: int = 50):
+                         margin: float = 1e-4, counts=None, max_rounds: int = 50,
+                         clusters: int = 0, sigma: float = 0.05):
     """Routing keys, queries and per-row thresholds for threshold mode.
 
     score_fn(q_row_f64, K_rows_f64) -> float64 scores; the caller supplies
     it (the oracle's scoring), so this module does no scoring itself.
     tau_b is the midpoint between the c_b-th and (c_b+1)-th largest scores,
     then any key within `margin` of tau_b is redrawn (seeded) until none is.
+    Keys are N(0, 1), or with clusters > 0 a mixture: each sequence draws
+    `clusters` centers ~ N(0, 1) and every key is a uniformly chosen center
+    plus sigma * N(0, 1) (a redrawn key keeps its center).  Trained models'
+    keys cluster (the structure an index over them relies on); Gaussian keys
+    do not, and the mixture stands in for the former.
     Returns (K_idx [B, n_cap, d], q_idx [B, 1, d], tau [B, 1] float32).
     Generation runs on the CPU; move the tensors afterwards.
     """
@@ -229,8 +235,15 @@ def gen_threshold_inputs(wl: Workload, score_fn, device="cpu", seed: int | None 
 
     base = wl.base_seed if seed is None else seed
     dt = torch_dtype(wl.dtype)
-    g = make_generator("cpu", seed_of(base, "K_idx"))
-    K = torch.randn((wl.B, wl.n_cap, wl.d), generator=g).to(dt)
+    g = make_generator("cpu", seed_of(base, "K_idx", clusters, sigma) if clusters else
+                       seed_of(base, "K_idx"))
+    if clusters > 0:
+        cent = torch.randn((wl.B, clusters, wl.d), generator=g)
+        assign = torch.randint(0, clusters, (wl.B, wl.n_cap), generator=g)
+        K = torch.gather(cent, 1, assign[..., None].expand(-1, -1, wl.d))
+        K = (K + sigma * torch.randn((wl.B, wl.n_cap, wl.d), generator=g)).to(dt)
+    else:
+        K = torch.randn((wl.B, wl.n_cap, wl.d), generator=g).to(dt)
     gq = make_generator("cpu", seed_of(base, "q_idx", 0))
     q = (torch.randn((wl.B, 1, wl.d), generator=gq) / math.sqrt(wl.d)).to(dt)
     cnt = threshold_counts(wl.B) if counts is None else list(counts)
@@ -249,7 +262,10 @@ def gen_threshold_inputs(wl: Workload, score_fn, device="cpu", seed: int | None 
             near = np.flatnonzero(np.abs(s - t64) < margin)
             if near.size == 0:
                 break
-            fresh = torch.randn((near.size, wl.d), generator=gr).to(dt)
+            fresh = torch.randn((near.size, wl.d), generator=gr)
+            if clusters > 0:
+                fresh = cent[b, assign[b, torch.from_numpy(near)]] + sigma * fresh
+            fresh = fresh.to(dt)
             K[b, torch.from_numpy(near)] = fresh
             s[near] = score_fn(qb, fresh.to(torch.float64).numpy())
         else:

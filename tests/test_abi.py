@@ -191,3 +191,59 @@ def test_route_static_limit_is_the_workspace_size(lib):
     assert lib.clsa_route_workspace_size(146, 1, 64, 131072, 2048, 2048, BF16) <= limit
     assert lib.clsa_route_workspace_size(147, 1, 64, 131072, 2048, 2048, BF16) > limit
     assert lib.clsa_status_string(SCRATCH_LIMIT) == b"shapes exceed the static scratch array"
+
+
+# ----------------------------------------------------------- Louver index
+def _bounds(*b):
+    return (ctypes.c_int64 * len(b))(*b)
+
+
+def test_louver_sizes(lib):
+    f = lib.clsa_louver_index_bytes
+    assert f(16, 128, 131072, 1, 64) > 16 * 131072 * 4  # perm alone
+    assert f(16, 128, 131072, 4, 64) > f(16, 128, 131072, 1, 64)  # cluster ids per subspace
+    for bad in ((0, 128, 1000, 1, 64), (1, 48, 1000, 1, 64), (1, 128, 1000, 3, 64),
+                (1, 32, 1000, 8, 64), (1, 128, 1000, 1, 4), (1, 128, 1000, 1, 300),
+                (1, 128, 0, 1, 64), (1, 128, (1 << 24) + 1, 1, 64)):
+        assert f(*bad) == 0, bad
+    assert lib.clsa_louver_build_workspace_size(2, 64, 5000, 2, 32) >= 3 * 2 * 2 * 5000 * 4
+    q = lib.clsa_louver_query_workspace_size
+    assert q(4, 64, 9000, 1, 64, 8000, 2, _bounds(0, 5000, 8000)) > 0
+    assert q(4, 64, 9000, 1, 64, 8000, 2, _bounds(0, 5000, 5000)) == 0  # empty segment
+    assert q(4, 64, 9000, 1, 64, 8000, 1, _bounds(1, 5000)) == 0        # must start at 0
+    assert q(4, 64, 9000, 1, 8, 8000000, 1, _bounds(0, 8000000)) == 0   # > 8192 clusters
+
+
+def _lv_build(lib, K=FAKE, B=2, d=64, n_cap=9000, dt=BF16, S=1, r=64, n_max=8000,
+              bounds=(0, 5000), index=FAKE, index_bytes=1 << 40, ws=FAKE, ws_bytes=1 << 40):
+    return lib.clsa_louver_build(K, B, d, n_cap, dt, S, r, n_max, len(bounds) - 1,
+                                 _bounds(*bounds), index, index_bytes, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(K=NULL), INVALID), (dict(index=NULL), INVALID), (dict(dt=F32), DTYPE),
+    (dict(S=3), INVALID), (dict(d=48), INVALID), (dict(r=4), INVALID),
+    (dict(bounds=(1, 5000)), INVALID), (dict(bounds=(0, 5000, 4000)), INVALID),
+    (dict(bounds=(0, 8001)), INVALID), (dict(n_cap=4000), INVALID),
+    (dict(index_bytes=1024), INVALID), (dict(ws=NULL), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
+])
+def test_louver_build_rejects(lib, kw, want):
+    assert _lv_build(lib, **kw) == want
+
+
+def _lv_query(lib, q=FAKE, K=FAKE, B=2, d=64, n_cap=9000, tau=FAKE, dt=BF16, S=1, r=64,
+              n_max=8000, bounds=(0, 5000), index=FAKE, mode=1, idx=FAKE, counts=FAKE, cap=64,
+              ws=FAKE, ws_bytes=1 << 40):
+    return lib.clsa_louver_query(q, K, B, d, n_cap, NULL, tau, dt, S, r, n_max, len(bounds) - 1,
+                                 _bounds(*bounds), index, mode, idx, counts, cap, NULL, ws,
+                                 ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(q=NULL), INVALID), (dict(tau=NULL), INVALID), (dict(index=NULL), INVALID),
+    (dict(idx=NULL), INVALID), (dict(cap=0), INVALID), (dict(mode=3), INVALID),
+    (dict(dt=F32), DTYPE), (dict(bounds=(0, 9500)), INVALID), (dict(S=4, d=16), INVALID),
+    (dict(ws=NULL), WORKSPACE), (dict(ws_bytes=100), WORKSPACE),
+])
+def test_louver_query_rejects(lib, kw, want):
+    assert _lv_query(lib, **kw) == want

@@ -1,0 +1,149 @@
+"""GPU parity of the Louver index (clsa_louver_build / clsa_louver_query)
+against the CPU oracle's exact threshold selection.
+
+Louver summary, gist.science, sections "2. Louver インデックス" and
+"クエリアルゴリズム": both query algorithms return every key scoring >= tau
+(no false negatives) and, since survivors are checked exactly, no other.
+Acceptance: the index sets equal the oracle's threshold sets bit for bit,
+with the true counts, on inputs whose scores all lie at least 1e-4 from tau
+(as for clsa_route_threshold).  Also checked: the number of keys the query
+scored exactly lies between the set size and the visible keys, and on
+clustered keys it is a small part of them (the index prunes).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_routing_amd import binding as clsa
+from long_context_sparse_routing_amd import inputs as gen
+from oracle import clsa_oracle as O
+from tests.parity_util import f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _score_fn(qq, KK):
+    return O.route_scores(qq, KK, KK.shape[0])
+
+
+def _taus(q, K, n_ctx, targets, margin=1e-4):
+    """tau per row between the c-th and (c+1)-th score, no score within margin."""
+    tau = np.zeros((len(n_ctx), 1), dtype=np.float32)
+    for b, n in enumerate(n_ctx):
+        s = O.route_scores(f64(q)[b, 0], f64(K)[b], n)
+        srt = np.sort(s)[::-1]
+        for c in range(targets[b], n):
+            t = np.float32(0.5 * (srt[c - 1] + srt[c])) if c > 0 else np.float32(srt[0] + 1)
+            if np.min(np.abs(s - float(t))) >= margin:
+                break
+        tau[b, 0] = t
+    return tau
+
+
+def _check(idx, counts, q, K, n_ctx, tau, cap):
+    o_idx, o_cnt = O.route_threshold(f64(q), f64(K), n_ctx, -1, tau, cap)
+    assert np.array_equal(counts.cpu().numpy(), o_cnt)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
+    return o_cnt
+
+
+@pytest.mark.parametrize("d,S", [(32, 1), (32, 4), (64, 1), (64, 2), (128, 1), (128, 4)])
+@pytest.mark.parametrize("r", [16, 64])
+def test_louver_small_segments_buffer_ragged(d, S, r):
+    g = torch.Generator()
+    g.manual_seed(600 + d + S + r)
+    B, n = 3, 5000
+    K = torch.randn((B, n, d), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, 1, d), generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    n_ctx = [5000, 4700, 4000]  # the last sequence ends inside the second segment
+    ix = clsa.LouverIndex(B, d, 4800, S=S, r=r, device=DEV)
+    Kd = K.to(DEV)
+    ix.build(Kd, 3000)
+    ix.build(Kd, 4500)  # the buffer of appended keys clustered into a second segment
+    tau = _taus(q, K, n_ctx, [1, 40, 700])
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    for mode in (1, 2):
+        for cap in (1024, 30):
+            chk = torch.zeros(B, dtype=torch.int32, device=DEV)
+            idx, counts, _ = ix.query(q.to(DEV), Kd, torch.from_numpy(tau).to(DEV), cap,
+                                      mode=mode, n_ctx=nc, checked=chk)
+            torch.cuda.synchronize()
+            o_cnt = _check(idx, counts, q, K, n_ctx, tau, cap)
+            c = chk.cpu().numpy()
+            assert np.all(c >= o_cnt) and np.all(c <= np.array(n_ctx)), (c, o_cnt)
+
+
+def test_louver_matches_threshold_route_and_is_deterministic():
+    g = torch.Generator()
+    g.manual_seed(650)
+    B, n, d = 2, 20000, 64
+    K = torch.randn((B, n, d), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, 1, d), generator=g) / 8).to(torch.bfloat16)
+    tau = torch.from_numpy(_taus(q, K, [n, n], [256, 3000])).to(DEV)
+    Kd, qd = K.to(DEV), q.to(DEV)
+    a = clsa.LouverIndex(B, d, n, S=2, r=32, device=DEV)
+    a.build(Kd, n)
+    b = clsa.LouverIndex(B, d, n, S=2, r=32, device=DEV)
+    b.build(Kd, n)
+    torch.cuda.synchronize()
+    assert torch.equal(a.buf, b.buf)  # the build is deterministic, bit for bit
+    ref = clsa.route_threshold(qd, Kd, tau, 4096)
+    for mode in (1, 2):
+        got = a.query(qd, Kd, tau, 4096, mode=mode)
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+
+
+def test_louver_duplicated_keys_and_extreme_thresholds():
+    # identical keys (zero-radius clusters, equal projections at every split)
+    # and thresholds above every score / below every score
+    g = torch.Generator()
+    g.manual_seed(660)
+    base = torch.randn((23, 64), generator=g).to(torch.bfloat16)
+    K = base[torch.randint(0, 23, (2, 6000), generator=g)]
+    q = (torch.randn((2, 1, 64), generator=g) / 8).to(torch.bfloat16)
+    s = [O.route_scores(f64(q)[b, 0], f64(K)[b], 6000) for b in range(2)]
+    tau = np.array([[np.float32(s[0].max() + 1)], [np.float32(s[1].min() - 1)]], dtype=np.float32)
+    ix = clsa.LouverIndex(2, 64, 6000, S=1, r=64, device=DEV)
+    ix.build(K.to(DEV), 6000)
+    for mode in (1, 2):
+        idx, counts, _ = ix.query(q.to(DEV), K.to(DEV), torch.from_numpy(tau).to(DEV), 6000,
+                                  mode=mode)
+        torch.cuda.synchronize()
+        assert counts.cpu().tolist() == [[0], [6000]]
+        _check(idx, counts, q, K, [6000, 6000], tau, 6000)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("clusters", [0, 64])
+def test_louver_threshold_workload(clusters):
+    """The threshold workload's shapes (16 sequences x 128K keys, d_idx 128,
+    256 .. 8192 keys per row), on its Gaussian keys and on clustered keys:
+    every query mode and subspace count returns the oracle's sets."""
+    wl = gen.WORKLOADS["threshold_128k_b16"]
+    K_cpu, q_cpu, tau = gen.gen_threshold_inputs(wl, _score_fn, clusters=clusters)
+    o_idx, o_cnt = O.route_threshold(f64(q_cpu), f64(K_cpu), [wl.n_ctx] * wl.B, -1,
+                                     tau.numpy(), 16384)
+    Kd, qd, taud = K_cpu.to(DEV), q_cpu.to(DEV), tau.to(DEV)
+    frac = {}
+    for S in (1, 4):
+        ix = clsa.LouverIndex(wl.B, wl.d, wl.n_ctx, S=S, r=64, device=DEV)
+        ix.build(Kd, wl.n_ctx)
+        for mode in (1, 2):
+            chk = torch.zeros(wl.B, dtype=torch.int32, device=DEV)
+            idx, counts, _ = ix.query(qd, Kd, taud, 16384, mode=mode, checked=chk)
+            torch.cuda.synchronize()
+            assert np.array_equal(counts.cpu().numpy(), o_cnt)
+            assert np.array_equal(idx.cpu().numpy(), o_idx)
+            frac[(S, mode)] = float(chk.sum()) / (wl.B * wl.n_ctx)
+        del ix
+    print(f"louver keep fraction (clusters={clusters}): {frac}", flush=True)
+    if clusters:
+        assert frac[(1, 1)] < 0.5, frac  # the index prunes on clustered keys
+    del Kd
+    torch.cuda.empty_cache()
