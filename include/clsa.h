@@ -113,8 +113,9 @@ const char* clsa_status_string(int status);
  * Other bf16 rows with k <= 2048 and n_cap <= 512K (decode: one query per
  * sequence) first score up to 4096 evenly spaced keys for a per-row lower
  * bound of the k-th score, then stream every visible key once and keep only
- * those at or above it; the workspace holds about 56 KB per row whatever
- * n_cap is.  A row whose bound keeps fewer than k keys, or more than 6144,
+ * those at or above it; the workspace holds about 72 KB per row whatever
+ * n_cap is (up to 512K).  A row whose bound keeps fewer than k keys, more
+ * than 6144, or more than one chunk's share of the candidate entries,
  * is redone exactly (much slower, results unchanged).  Other rows (fp32, or
  * k > 2048) keep every key's score in the workspace (12 bytes per key).
  * Errors: CLSA_ERR_INVALID (null pointer, B/M/k < 1, d unsupported,
@@ -142,8 +143,8 @@ int clsa_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64_
  * device, on the first call there).
  * Shapes whose clsa_route_workspace_size exceeds CLSA_STATIC_SCRATCH_BYTES
  * are rejected with CLSA_ERR_SCRATCH_LIMIT before anything is enqueued:
- * with bf16 keys and k <= 2048, up to 146 decode rows (M = 1) at any context
- * length up to 512K fit.
+ * with bf16 keys and k <= 2048, at least 109 decode rows (M = 1) fit at any
+ * context length up to 512K (113 at 128K).
  * Every call on one GPU uses that GPU's one array, which keeps the previous
  * call's contents (the kernels clear what they need zeroed): calls that
  * overlap on one GPU (different streams, or different host threads without

@@ -159,6 +159,14 @@ CLSA_DEV int sample_rank(int64_t n, int64_t k, int ns) {
   return (int)ceilf(sr * sr);
 }
 
+// Candidate segments of the decode-row filter: a row owns C x segcap
+// entries, shared evenly by its cv visible chunks (chunk c's segment starts
+// at c x the share); a chunk never holds more candidates than its CH keys.
+CLSA_DEV uint32_t row_seg_cap(int C, int segcap, int CH, int64_t cv) {
+  const int64_t c = (int64_t)C * segcap / (cv < 1 ? 1 : cv);
+  return (uint32_t)(c < CH ? c : CH);
+}
+
 // Samples per row of the decode-row threshold estimate (at most), and how
 // many of each 64 consecutive samples' largest key prefixes are kept.
 constexpr int kRowSamples = 4096;

@@ -71,6 +71,7 @@ struct BlockArgs {
   int kc;                  // keys per chunk (chunk_keys(d))
   int nchunks;             // key chunks per row
   int rows_pg;             // rows per filter workgroup (multiple of 64)
+  int segcap;              // decode rows: candidate entries per chunk and row (row_seg_cap)
   float* thr;              // [R] filter threshold; -inf: every key, +inf: none
   uint32_t* segcnt;        // [R][nchunks] candidates per segment
   uint64_t* seg;           // [R][nchunks][kc]: position | (score - T') << 32
@@ -347,7 +348,6 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
 // samples on the matrix cores (one per thread) and store their 16-bit key
 // prefixes -- each wave's kRowTop largest when the plan is compact, else
 // all of them -- for the score pass, which ranks them (rank_row_samples).
-// The first workgroup of each row also zeroes the row's candidate count.
 constexpr int kRowNs = kRowSamples;
 constexpr int kRowSampleWG = kRowNs / kNT;  // one sample per thread
 
@@ -355,7 +355,6 @@ template <int D>
 __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
   const int r = blockIdx.y, b = r / a.M, m = r % a.M;
   const int lane = lane_id(), w = threadIdx.x / kWave;
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.segcnt[r] = 0u;  // the filter's candidate count
   const int64_t n_vis = row_visible(a, b, m);
   const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
   if (k_eff >= n_vis) return;  // the select takes every visible key
@@ -824,14 +823,17 @@ inline size_t select_lds_bytes(int64_t n_cap) {
   return (size_t)select_words_per_thread(n_cap) * kNT * sizeof(uint32_t) * 5 / 4;
 }
 
-// CONTIG: the row's candidates are one contiguous list of segcnt[r] entries
-// at seg + r * kSelCap (the decode-row filter); otherwise a.nchunks
-// segments of a.kc entries each, segcnt[r][c] used.
-template <int D, bool CONTIG>
+// The row's candidates sit in segments, one per key chunk, with
+// segcnt[r][c] entries each.  Block routing (ROWSEG false): a.nchunks
+// segments of a.kc entries, one per chunk of a.kc keys.  Decode rows
+// (ROWSEG true): a row owns a.nchunks x a.segcap entries, shared by its
+// visible chunks of a.kc keys (row_seg_cap); a count above that share means
+// the segment overflowed, and the row is rescanned.
+template <int D, bool ROWSEG>
 __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   extern __shared__ u32x4_t bitmap4[];  // select_lds_bytes(n_cap): bitmap, then group prefixes
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(bitmap4);
-  __shared__ uint32_t segoff[CONTIG ? 1 : kMaxSegs + 1];
+  __shared__ uint32_t segoff[kMaxSegs + 1];
   __shared__ SelScratch S;
   __shared__ uint32_t wcnt[kNT / kWave];
 
@@ -854,21 +856,18 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   for (int i = w0; i < w0 + wpt; i += 4) bitmap4[i / 4] = u32x4_t{0u, 0u, 0u, 0u};
 
   // offsets of the row's segments (one per key chunk)
-  const int nseg = CONTIG ? 1 : a.nchunks;
-  uint32_t n_c;
-  uint64_t pre[CONTIG ? kPerT : 1];  // contiguous list: every slot loaded with the count
-  if constexpr (CONTIG) {
-    const uint64_t* row = a.seg + (size_t)r * kSelCap;
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) pre[u] = row[u * kNT + tid];
-    n_c = a.segcnt[r];  // the true count, even past the list's capacity
-  } else {
-    n_c = block_excl_scan_arr(a.segcnt + (size_t)r * nseg, segoff, nseg, S.tmp, S.bc);
-    if (tid == 0) segoff[nseg] = n_c;
-    __syncthreads();
-  }
+  const int nseg = ROWSEG ? (int)ceil_div64(n_vis, a.kc) : a.nchunks;
+  const uint32_t half =  // segment capacity
+      ROWSEG ? row_seg_cap(a.nchunks, a.segcap, a.kc, nseg) : (uint32_t)a.kc;
+  const uint32_t* cnt_row = a.segcnt + (size_t)r * a.nchunks;
+  const uint32_t n_c = block_excl_scan_arr(cnt_row, segoff, nseg, S.tmp, S.bc);
+  bool over = false;
+  if constexpr (ROWSEG)
+    for (int i = tid; i < nseg; i += kNT) over = over || cnt_row[i] > half;
+  if (tid == 0) segoff[nseg] = n_c;
+  const bool overflow = __syncthreads_or(over ? 1 : 0) != 0;
 
-  if (n_c < (uint32_t)k_eff || n_c > (uint32_t)kSelCap) {
+  if (n_c < (uint32_t)k_eff || n_c > (uint32_t)kSelCap || overflow) {
     exact_rescan<D>(a, b, m, n_vis, k_eff, out, S.h, S.tmp, S.bc, wcnt);
     return;
   }
@@ -879,14 +878,7 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
   // all of the thread's searches in step so that each step waits on LDS once.
   const int cnt = (int)((n_c + kNT - 1 - (uint32_t)tid) / kNT);  // elements of this thread
   uint32_t key[kPerT], pos[kPerT];
-  if constexpr (CONTIG) {
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) {
-      key[u] = score_key(__uint_as_float((uint32_t)(pre[u] >> 32)));
-      pos[u] = (uint32_t)pre[u];
-    }
-  } else {
-    const uint32_t half = (uint32_t)a.kc;  // segment capacity
+  {
     int lo[kPerT];
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) lo[u] = 0;
@@ -907,7 +899,8 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
 #pragma unroll
     for (int u = 0; u < kPerT; ++u)
       off[u] = (uint32_t)lo[u] * half + ((uint32_t)(u * kNT + tid) - segoff[lo[u]]);
-    const uint64_t* rowseg = a.seg + (size_t)r * nseg * half;
+    const uint64_t* rowseg =
+        a.seg + (size_t)r * (ROWSEG ? (size_t)a.nchunks * a.segcap : (size_t)nseg * half);
     uint64_t e[kPerT];
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) e[u] = u < cnt ? rowseg[off[u]] : 0ull;
@@ -1109,27 +1102,27 @@ BlockArgs seg_args(const void* q_idx, const void* K_idx, int B, int M, int64_t n
 }  // namespace
 
 void seg_route_sample(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
-                      const int32_t* n_ctx, int64_t q_pos0, int k, uint16_t* samp,
-                      uint32_t* rowcnt, hipStream_t s) {
+                      const int32_t* n_ctx, int64_t q_pos0, int k, uint16_t* samp, hipStream_t s) {
   BlockArgs a = seg_args(q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, k);
-  a.segcnt = rowcnt;
   const dim3 grid((unsigned)kRowSampleWG, (unsigned)(B * M));
   if (d == 32) hipLaunchKernelGGL(row_sample<32>, grid, dim3(kNT), 0, s, a, samp);
   else if (d == 64) hipLaunchKernelGGL(row_sample<64>, grid, dim3(kNT), 0, s, a, samp);
   else hipLaunchKernelGGL(row_sample<128>, grid, dim3(kNT), 0, s, a, samp);
 }
 
-int seg_route_list_cap() { return kSelCap; }
-
 void seg_route_select(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
                       const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
-                      int cap, uint32_t* rowcnt, uint64_t* cand, hipStream_t s) {
+                      int cap, int chunk_keys, int nchunks, int segcap, uint32_t* segcnt,
+                      uint64_t* seg, hipStream_t s) {
   BlockArgs a = seg_args(q_idx, K_idx, B, M, n_cap, n_ctx, q_pos0, k);
   a.idx = idx;
   a.counts = counts;
   a.cap = cap;
-  a.segcnt = rowcnt;
-  a.seg = cand;
+  a.kc = chunk_keys;
+  a.nchunks = nchunks;
+  a.segcap = segcap;
+  a.segcnt = segcnt;
+  a.seg = seg;
   const dim3 grid((unsigned)(B * M));
   const size_t lds = select_lds_bytes(n_cap);
   if (d == 32) hipLaunchKernelGGL((block_select<32, true>), grid, dim3(kNT), lds, s, a);

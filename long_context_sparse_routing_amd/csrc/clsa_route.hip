@@ -46,7 +46,6 @@
 #include "clsa_common.h"
 
 namespace clsa {
-int seg_route_list_cap();  // candidates a decode-row list holds (clsa_prefill.hip)
 
 namespace {
 
@@ -84,9 +83,9 @@ struct RouteArgs {
   uint64_t* cand;         // [R][n_cap]  chunk c's candidates at [c*CH, ...)
   // filter mode
   const uint16_t* samp;   // [R][kRowSamples] sampled key prefixes (row_sample)
-  uint32_t* rowcnt;       // [R]        candidates found (zeroed by the sampling kernel)
-  uint64_t* clist;        // [R][lcap]  position | score bits << 32, the first lcap kept
-  int lcap;
+  uint32_t* segcnt;       // [R][C]     candidates found per chunk (true count)
+  uint64_t* seg;          // [R][C * segcap] position | score bits << 32, per chunk
+  int segcap;             // entries per chunk and row (shared by visible chunks)
 };
 
 CLSA_DEV int64_t visible(const RouteArgs& a, int r) {
@@ -311,17 +310,18 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
   }
 
   if (MODE == kFilter) {
-    // the chunk's candidates, appended to the row's list (one reservation
-    // per workgroup; entries past the list's capacity are counted, not kept)
+    // the chunk's candidates into its own segment of the row, with the true
+    // count (entries past the segment are counted, not kept).  No atomics
+    // between workgroups: a device-scope reservation on one counter per row
+    // cost every workgroup a round trip at its end (scan 26 -> 21 us at
+    // 8 rows of 128K keys without it).
     __syncthreads();
     const uint32_t n = ccount;
-    if (n == 0u) return;
-    if (tid == 0) tmp[0] = atomicAdd(&a.rowcnt[r], n);
-    __syncthreads();
-    const uint32_t base = tmp[0];
-    uint64_t* dst = a.clist + (size_t)r * a.lcap;
-    for (uint32_t i = tid; i < n; i += kNT)
-      if (base + i < (uint32_t)a.lcap) dst[base + i] = cbuf[i];
+    const uint32_t cap = row_seg_cap(a.C, a.segcap, a.CH, chunks_of(n_vis, a.CH));
+    if (tid == 0) a.segcnt[(size_t)r * a.C + c] = n;
+    uint64_t* dst = a.seg + (size_t)r * a.C * a.segcap + (size_t)c * cap;
+    const uint32_t m = n < cap ? n : cap;
+    for (uint32_t i = tid; i < m; i += kNT) dst[i] = cbuf[i];
   } else if (TOPK) {
     __syncthreads();
     uint32_t* gh = a.ghist + (size_t)r * kBuckets;
@@ -717,10 +717,14 @@ void launch_score(const RouteArgs& a, clsa_dtype dt, int d, dim3 grid, hipStream
 
 // Filter path workspace: keys per chunk chosen so that the score pass has
 // at least about a thousand workgroups (256 .. 2048 keys, a multiple of the
-// block; 8 rows at 128K take 1024-key chunks, 32 rows 2048);
-// per row the samples, the candidate count and the candidate list.
+// block; 8 rows at 128K take 1024-key chunks, 32 rows 2048); per row the
+// samples, a candidate count per chunk and C x segcap candidate entries.
+// segcap gives a row at least 8192 entries (the select takes at most 6144)
+// and every chunk at least 32: a full row at 128K expects about 28 per
+// 1024-key chunk against a share of 64; shorter rows share the same
+// entries among fewer chunks.
 struct FilterLayout {
-  int CH, C;
+  int CH, C, segcap;
   size_t o_samp, o_cnt, o_cand, total;
 };
 
@@ -730,10 +734,13 @@ FilterLayout filter_layout(int64_t R, int64_t n_cap) {
   while (CH > kNT && R * ceil_div64(n_cap, CH) < 1024) CH /= 2;
   L.CH = (int)CH;
   L.C = (int)ceil_div64(n_cap, CH);
+  int64_t sc = ceil_div64(8192, L.C);
+  if (sc < 32) sc = 32;
+  L.segcap = (int)(sc < CH ? sc : CH);
   size_t o = 0;
   L.o_samp = o; o = align_up(o + (size_t)R * kRowSamples * 2, 256);
-  L.o_cnt = o; o = align_up(o + (size_t)R * 4, 256);
-  L.o_cand = o; o = align_up(o + (size_t)R * seg_route_list_cap() * 8, 256);
+  L.o_cnt = o; o = align_up(o + (size_t)R * L.C * 4, 256);
+  L.o_cand = o; o = align_up(o + (size_t)R * L.C * L.segcap * 8, 256);
   L.total = o;
   return L;
 }
@@ -780,11 +787,11 @@ int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64
 // Threshold and select of the filter path (clsa_prefill.hip).
 bool seg_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt);
 void seg_route_sample(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
-                      const int32_t* n_ctx, int64_t q_pos0, int k, uint16_t* samp,
-                      uint32_t* rowcnt, hipStream_t s);
+                      const int32_t* n_ctx, int64_t q_pos0, int k, uint16_t* samp, hipStream_t s);
 void seg_route_select(const void* q_idx, const void* K_idx, int B, int M, int d, int64_t n_cap,
                       const int32_t* n_ctx, int64_t q_pos0, int k, int32_t* idx, int32_t* counts,
-                      int cap, uint32_t* rowcnt, uint64_t* cand, hipStream_t s);
+                      int cap, int chunk_keys, int nchunks, int segcap, uint32_t* segcnt,
+                      uint64_t* seg, hipStream_t s);
 }  // namespace clsa
 
 using namespace clsa;
@@ -839,14 +846,14 @@ int route_call(const void* q_idx, const void* K_idx, int B, int M, int d, int64_
     a.CH = F.CH;
     a.C = F.C;
     a.samp = reinterpret_cast<const uint16_t*>(base + F.o_samp);
-    a.rowcnt = reinterpret_cast<uint32_t*>(base + F.o_cnt);
-    a.clist = reinterpret_cast<uint64_t*>(base + F.o_cand);
-    a.lcap = seg_route_list_cap();
+    a.segcnt = reinterpret_cast<uint32_t*>(base + F.o_cnt);
+    a.seg = reinterpret_cast<uint64_t*>(base + F.o_cand);
+    a.segcap = F.segcap;
     seg_route_sample(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k,
-                     reinterpret_cast<uint16_t*>(base + F.o_samp), a.rowcnt, s);
+                     reinterpret_cast<uint16_t*>(base + F.o_samp), s);
     launch_score<kFilter>(a, dt, d, dim3((unsigned)F.C, (unsigned)R), s);
-    seg_route_select(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, a.rowcnt,
-                     a.clist, s);
+    seg_route_select(q_idx, K_idx, B, M, d, n_cap, n_ctx, q_pos0, k, idx, counts, cap, F.CH, F.C,
+                     F.segcap, a.segcnt, a.seg, s);
     return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
   }
   const Layout L = make_layout(R, n_cap, true);

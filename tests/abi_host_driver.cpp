@@ -128,7 +128,7 @@ void route_rejects() {
   EXPECT(clsa_route_static(kFake, kFake, 1, 1, 64, 4096, nullptr, -1, 256,
                            static_cast<clsa_dtype>(5), fi, fi, 256, nullptr) ==
          CLSA_ERR_UNSUPPORTED_DTYPE);
-  EXPECT(clsa_route_static(kFake, kFake, 147, 1, 64, 131072, nullptr, -1, 2048, CLSA_BF16, fi, fi,
+  EXPECT(clsa_route_static(kFake, kFake, 114, 1, 64, 131072, nullptr, -1, 2048, CLSA_BF16, fi, fi,
                            2048, nullptr) == CLSA_ERR_SCRATCH_LIMIT);
   EXPECT(clsa_route_static(kFake, kFake, 1, 4096, 64, 131072, nullptr, -1, 2048, CLSA_BF16, fi,
                            fi, 2048, nullptr) == CLSA_ERR_SCRATCH_LIMIT);

@@ -52,14 +52,14 @@ def test_static_route_matches_route(first, second):
 
 
 def test_static_route_rejects_shapes_past_the_scratch_limit():
-    q, K = _inputs(5, 1, 1, 1000, 64, torch.bfloat16)
-    qq = q.expand(147, 1, 64).contiguous()
-    KK = K.expand(147, 1000, 64).contiguous()
+    # decode rows at 128K keys, k = 2048: 113 rows fit the array, 114 do not
+    q, K = _inputs(5, 1, 1, 131072, 64, torch.bfloat16)
+    qq = q.expand(114, 1, 64).contiguous()
+    KK = K.expand(114, 131072, 64).contiguous()
     with pytest.raises(clsa.ClsaError) as e:
-        clsa.route_static(qq, KK, 256)
+        clsa.route_static(qq, KK, 2048)
     assert e.value.status == -5
-    # 146 decode rows still fit
-    idx, cnt = clsa.route_static(qq[:146], KK[:146], 256)
+    idx, cnt = clsa.route_static(qq[:113], KK[:113], 2048)
     torch.cuda.synchronize()
-    ref_idx, _ = clsa.route(qq[:146], KK[:146], 256)
+    ref_idx, _ = clsa.route(qq[:113], KK[:113], 2048)
     assert torch.equal(idx, ref_idx)
