@@ -539,6 +539,74 @@ def louver_leg(dev, reps):
     return out
 
 
+def alt_routers_leg(dev, reps):
+    """The two alternative ways to produce the shared list, on the headline
+    decode shapes (8 sequences x 128K keys, d_idx 64, k 2048), against the
+    shared routing call:
+      centroid table (CSAttention summary): k-means of 4096 prompt routing
+        queries per sequence into 64 centroids, each with its top-2048 keys
+        (built once, at prefill); a decode query scores its 3 best
+        centroids' rows (6144 keys) instead of all 128K;
+      cross-layer aggregation (CLAA abstract): the top-k of 16 layers' index
+        head scores summed, i.e. 16 index heads scanned per token.
+    Reports times, bytes read, and the overlap of each list with the exact
+    shared top-k (a diagnostic of what the cheaper lookup gives up)."""
+    import torch
+    from long_context_sparse_routing_amd import binding as clsa
+    from long_context_sparse_routing_amd import inputs as gen
+    wl = gen.WORKLOADS["decode_128k_b8"]
+    n = wl.n_ctx
+    K_idx, u, _ = gen.gen_routing_keys(wl, dev)
+    nc = torch.full((wl.B,), n, dtype=torch.int32, device=dev)
+    q_idx = gen.gen_routing_query(wl, u, 0, dev)
+    shared = clsa.prepare_route(q_idx, K_idx, wl.k, n_ctx=nc)
+    ex_idx = shared()[0].clone()
+    shared_ms = _event_ms(shared, reps)
+    qp = gen.gen_prompt_routing_queries(wl, u, 4096, dev)
+    C, T, P, rounds = 64, 2048, 3, 8
+    clsa.csa_build(qp, K_idx, C, T, rounds=rounds, n_ctx=nc)  # kernels load
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cent, table = clsa.csa_build(qp, K_idx, C, T, rounds=rounds, n_ctx=nc)
+    e1.record()
+    torch.cuda.synchronize()
+    build_ms = e0.elapsed_time(e1)
+    look = clsa.prepare_csa_route(q_idx, K_idx, cent, table, n, P, wl.k, n_ctx=nc)
+    c_idx = look()[0]
+    csa_ms = _event_ms(look, reps)
+    overlap = lambda a: [len(set(a[b, 0].tolist()) & set(ex_idx[b, 0].tolist())) / wl.k  # noqa: E731
+                         for b in range(wl.B)]
+    csa_bytes = wl.B * (C * wl.d * 2 + P * T * (4 + wl.d * 2))
+    out = {"workload": wl.name, "shared_route_ms": shared_ms,
+           "centroid_table": {"C": C, "T": T, "P": P, "kmeans_rounds": rounds,
+                              "prompt_queries": 4096, "build_ms": build_ms, "route_ms": csa_ms,
+                              "speedup_vs_shared": shared_ms / csa_ms, "bytes": csa_bytes,
+                              "recall_of_exact_topk": overlap(c_idx.cpu())}}
+    del cent, table, look, qp
+    # cross-layer aggregation: one index head per layer
+    H = wl.L
+    wl_h = wl.with_(name=wl.name + "_layer_heads", B=H * wl.B, base_seed=wl.base_seed + 100)
+    Kh, uh, _ = gen.gen_routing_keys(wl_h, dev)
+    qh = gen.gen_routing_query(wl_h, uh, 0, dev)
+    Kh = Kh.view(H, wl.B, wl.n_cap, wl.d)
+    qh = qh.view(H, wl.B, 1, wl.d)
+    agg = clsa.prepare_route_aggregated(qh, Kh, wl.k, n_ctx=nc)
+    agg()
+    agg_ms = _event_ms(agg, max(1, reps // 2))
+    per = [clsa.prepare_route(qh[h], Kh[h], wl.k, n_ctx=nc) for h in range(H)]
+    per_ms = _event_ms(lambda: [c() for c in per], max(1, reps // 2))
+    agg_bytes = H * wl.B * n * wl.d * 2
+    out["cross_layer_aggregation"] = {
+        "heads": H, "route_ms": agg_ms, "bytes": agg_bytes,
+        "GBs": agg_bytes / (agg_ms * 1e-3) / 1e9, "per_layer_routing_ms": per_ms,
+        "vs_shared": agg_ms / shared_ms,
+        "note": "one shared list from 16 heads' summed scores; per-layer routing makes 16 lists"}
+    del Kh, qh, agg, per, K_idx
+    torch.cuda.empty_cache()
+    return out
+
+
 def tiny_fp32_step(dev, reps, cpu_budget=0.0):
     """The smallest configuration: one fp32 sequence at 4K context, d_idx 32,
     one layer with one head of dim 64, k = 256 -- a routing call plus an
@@ -849,6 +917,7 @@ def main():
         res["decode_32k"] = decode_32k_step(dev, 64, cb)
         res["tiny_fp32_4k"] = tiny_fp32_step(dev, 200, min(1.0, cb))
         res["louver"] = louver_leg(dev, 5)
+        res["alt_routers"] = alt_routers_leg(dev, 10)
     if args.prefill_calls > 0:
         res["prefill_routing"] = prefill_routing(args.prefill_calls, dev, min(5.0, args.cpu_budget),
                                                  bool(args.prefill_attention))

@@ -265,6 +265,67 @@ int clsa_louver_query(const void* q_idx, const void* K_idx, int B, int d, int64_
                       void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * clsa_route_aggregated - top-k routing of cross-layer aggregated scores.
+ * (CLAA abstract, fugumt.com, "CLAA: Cross-Layer Attention Aggregation for
+ * Accelerating LLM Prefill": token importance taken from single layers is
+ * unstable; aggregating it across layers ranks tokens stably.)
+ * H index heads (one per layer): q_idx and K_idx are HOST arrays of H device
+ * pointers, each laid out as in clsa_route; the score of key j for row
+ * (b, m) is sum_h q_idx[h][b][m] . K_idx[h][b][j] (fp32 sums of exact
+ * products), and the row's list is the top-k of that sum with clsa_route's
+ * rules and outputs.  1 <= H <= 64; the workspace is that of the exhaustive
+ * path (12 bytes per key and row).
+ * Errors: as clsa_route.
+ */
+size_t clsa_route_aggregated_workspace_size(int H, int B, int M, int d, int64_t n_cap, int k,
+                                            int cap, clsa_dtype dt);
+int clsa_route_aggregated(int H, const void* const* q_idx, const void* const* K_idx, int B, int M,
+                          int d, int64_t n_cap, const int32_t* n_ctx, int64_t q_pos0, int k,
+                          clsa_dtype dt, int32_t* idx, int32_t* counts, int cap, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Centroid table router - decode routing through a table built at prefill.
+ * (CSAttention summary, news.neo-ai.one: the queries of a long context
+ * cluster, so centroids predict which keys matter; prefill builds a
+ * fixed-size query-centroid lookup table per request and decoding consults
+ * it instead of scanning the whole context.)
+ *
+ * clsa_csa_build: for each sequence b, Lloyd's k-means over its M prefill
+ *   routing queries q_prefill [B][M][d] (bf16): centroid c starts at query
+ *   floor(c M / C); `rounds` rounds of nearest-centroid assignment (squared
+ *   Euclidean distance in fp32, ties to the lower centroid) and mean update
+ *   (an empty cluster keeps its centroid).  centroids [B][C][d] (bf16,
+ *   device, out) are the results rounded to bf16; table [B][C][T] (int32,
+ *   device, out) row c lists the T keys of K_idx [B][n_cap][d] that centroid
+ *   c scores highest, ascending (clsa_route's rules, over n_ctx[b] keys).
+ *   M >= C, 1 <= C <= 1024 with C * d <= 16384, 1 <= T <= 2048,
+ *   n_cap <= 512K, B * C <= 65535, rounds <= 100.
+ * clsa_csa_route: for each sequence b (q_idx [B][d]): the P (1 <= P <= 16)
+ *   centroids with the highest q . centroid (ties to the lower centroid);
+ *   the candidates are the keys of their table rows plus every position in
+ *   [n_table, n_ctx[b]) (keys appended since the table was built), keeping
+ *   positions below n_ctx[b]; the list is the top-k of the candidates'
+ *   exact scores (fp32 sums of exact products; ties to the lower position),
+ *   ascending, -1 padded to cap; counts[b] = min(k, candidates).  The table
+ *   is read as built by clsa_csa_build with the same B, d, C, T.
+ *   P * T + (n_cap - n_table) <= 8192 (rebuild the table as the buffer of
+ *   appended keys grows).
+ * Both calls: bf16 only (CLSA_ERR_UNSUPPORTED_DTYPE otherwise); device
+ * workspace of the matching *_workspace_size; errors CLSA_ERR_INVALID,
+ * CLSA_ERR_WORKSPACE, CLSA_ERR_HIP.
+ */
+size_t clsa_csa_build_workspace_size(int B, int M, int d, int64_t n_cap, int C, int T);
+int clsa_csa_build(const void* q_prefill, const void* K_idx, int B, int M, int d, int64_t n_cap,
+                   const int32_t* n_ctx, int C, int rounds, int T, clsa_dtype dt, void* centroids,
+                   int32_t* table, void* ws, size_t ws_bytes, void* stream);
+size_t clsa_csa_route_workspace_size(int B, int d, int64_t n_cap, int C, int T, int P);
+int clsa_csa_route(const void* q_idx, const void* K_idx, int B, int d, int64_t n_cap,
+                   const int32_t* n_ctx, const void* centroids, const int32_t* table, int C, int T,
+                   int64_t n_table, int P, int k, clsa_dtype dt, int32_t* idx, int32_t* counts,
+                   int cap, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * clsa_kv_append - write one new token's rows into preallocated caches.
  * (CLSA explainer, section "CLSAの仕組み": the self-decoder writes the KV
  * cache that every cross-decoder layer then reads.)  This is that per-step

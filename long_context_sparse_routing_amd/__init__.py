@@ -5,16 +5,21 @@ The compute path is libclsa.so (hand-written HIP for gfx950) behind a C ABI
 """
 from .binding import (  # noqa: F401
     ClsaError,
+    csa_build,
+    csa_route,
     LouverIndex,
     Prepared,
     kv_append,
     load_library,
+    prepare_csa_route,
     prepare_kv_append,
     prepare_route,
+    prepare_route_aggregated,
     prepare_route_static,
     prepare_route_threshold,
     prepare_sparse_attn,
     route,
+    route_aggregated,
     route_static,
     route_threshold,
     route_threshold_workspace_size,

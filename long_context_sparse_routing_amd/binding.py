@@ -80,6 +80,21 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.clsa_louver_query.restype = i32
     lib.clsa_louver_query.argtypes = [vp, vp, i32, i32, i64, vp, vp, i32, i32, i32, i64, i32, vp,
                                       vp, i32, vp, vp, i32, vp, vp, sz, vp]
+    lib.clsa_route_aggregated_workspace_size.restype = sz
+    lib.clsa_route_aggregated_workspace_size.argtypes = [i32, i32, i32, i32, i64, i32, i32, i32]
+    lib.clsa_route_aggregated.restype = i32
+    lib.clsa_route_aggregated.argtypes = [i32, vp, vp, i32, i32, i32, i64, vp, i64, i32, i32, vp,
+                                          vp, i32, vp, sz, vp]
+    lib.clsa_csa_build_workspace_size.restype = sz
+    lib.clsa_csa_build_workspace_size.argtypes = [i32, i32, i32, i64, i32, i32]
+    lib.clsa_csa_build.restype = i32
+    lib.clsa_csa_build.argtypes = [vp, vp, i32, i32, i32, i64, vp, i32, i32, i32, i32, vp, vp, vp,
+                                   sz, vp]
+    lib.clsa_csa_route_workspace_size.restype = sz
+    lib.clsa_csa_route_workspace_size.argtypes = [i32, i32, i64, i32, i32, i32]
+    lib.clsa_csa_route.restype = i32
+    lib.clsa_csa_route.argtypes = [vp, vp, i32, i32, i64, vp, vp, vp, i32, i32, i64, i32, i32, i32,
+                                   vp, vp, i32, vp, sz, vp]
     lib.clsa_kv_append.restype = i32
     lib.clsa_kv_append.argtypes = [i32, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, vp, i32,
                                    vp]
@@ -488,3 +503,103 @@ class LouverIndex:
               checked=None, ws=None, stream=None):
         return self.prepare_query(q_idx, K_idx, tau, cap, mode, n_ctx, idx, counts, checked, ws,
                                   stream)()
+
+
+def prepare_route_aggregated(q_idx, K_idx, k: int, n_ctx: torch.Tensor | None = None,
+                             q_pos0: int = -1, cap: int | None = None,
+                             idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                             ws: torch.Tensor | None = None, stream=None) -> Prepared:
+    """clsa_route_aggregated, marshalled.  q_idx: [H, B, M, d] tensor or list
+    of H [B, M, d]; K_idx: [H, B, n_cap, d] or list of H [B, n_cap, d].
+    Calling the result returns (idx [B, M, cap], counts [B, M])."""
+    lib = load_library()
+    ql, Kl = _layers(q_idx), _layers(K_idx)
+    H = len(ql)
+    _need(1 <= H <= MAX_LAYERS and len(Kl) == H, "q_idx and K_idx need the same 1..64 heads")
+    B, M, d, n_cap = _route_shapes(ql[0], Kl[0])
+    for h in range(H):
+        _check_shape(ql[h], (B, M, d), f"q_idx[{h}]")
+        _check_shape(Kl[h], (B, n_cap, d), f"K_idx[{h}]")
+        _need(ql[h].dtype == ql[0].dtype and Kl[h].dtype == ql[0].dtype,
+              "every head shares one dtype", TypeError)
+    cap = k if cap is None else cap
+    dev = ql[0].device
+    if idx is None:
+        idx = torch.empty((B, M, cap), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((B, M), dtype=torch.int32, device=dev)
+    _check_route_io(B, M, cap, n_ctx, idx, counts)
+    _check_dev(*ql, *Kl, n_ctx, idx, counts)
+    dt = _dt(ql[0])
+    ws = _workspace(lib.clsa_route_aggregated_workspace_size(H, B, M, d, n_cap, k, cap, dt), dev,
+                    ws)
+    arr = ctypes.c_void_p * H
+    qa = arr(*[t.data_ptr() for t in ql])
+    ka = arr(*[t.data_ptr() for t in Kl])
+    args = (H, qa, ka, B, M, d, n_cap, _ptr(n_ctx), q_pos0, k, dt, _ptr(idx), _ptr(counts), cap,
+            _ptr(ws), ws.numel(), _stream(stream))
+    return Prepared("clsa_route_aggregated", lib.clsa_route_aggregated, args, (idx, counts),
+                    (ql, Kl, n_ctx, idx, counts, ws, qa, ka))
+
+
+def route_aggregated(q_idx, K_idx, k: int, **kw):
+    return prepare_route_aggregated(q_idx, K_idx, k, **kw)()
+
+
+def csa_build(q_prefill: torch.Tensor, K_idx: torch.Tensor, C: int, T: int, rounds: int = 10,
+              n_ctx: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """clsa_csa_build: q_prefill [B, M, d], K_idx [B, n_cap, d] (bf16) ->
+    (centroids [B, C, d] bf16, table [B, C, T] int32)."""
+    lib = load_library()
+    B, M, d, n_cap = _route_shapes(q_prefill, K_idx)
+    _need(q_prefill.dtype == torch.bfloat16, "the centroid table router takes bfloat16", TypeError)
+    _check_i32(n_ctx, (B,), "n_ctx")
+    _check_dev(q_prefill, K_idx, n_ctx)
+    dev = q_prefill.device
+    cent = torch.empty((B, C, d), dtype=torch.bfloat16, device=dev)
+    table = torch.empty((B, C, T), dtype=torch.int32, device=dev)
+    need = lib.clsa_csa_build_workspace_size(B, M, d, n_cap, C, T)
+    _need(need > 0, f"unsupported centroid table shape B={B} M={M} d={d} C={C} T={T}")
+    ws = _workspace(need, dev, ws)
+    st = lib.clsa_csa_build(_ptr(q_prefill), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), C, rounds,
+                            T, CLSA_BF16, _ptr(cent), _ptr(table), _ptr(ws), ws.numel(),
+                            _stream(stream))
+    if st != 0:
+        raise ClsaError("clsa_csa_build", st)
+    return cent, table
+
+
+def prepare_csa_route(q_idx: torch.Tensor, K_idx: torch.Tensor, centroids: torch.Tensor,
+                      table: torch.Tensor, n_table: int, P: int, k: int,
+                      n_ctx: torch.Tensor | None = None, cap: int | None = None,
+                      idx: torch.Tensor | None = None, counts: torch.Tensor | None = None,
+                      ws: torch.Tensor | None = None, stream=None) -> Prepared:
+    """clsa_csa_route, marshalled: q_idx [B, 1, d]; calling the result
+    returns (idx [B, 1, cap], counts [B, 1])."""
+    lib = load_library()
+    B, M, d, n_cap = _route_shapes(q_idx, K_idx)
+    _need(M == 1, "the centroid table router takes one query row per sequence")
+    _need(centroids.dim() == 3 and table.dim() == 3, "centroids [B, C, d] and table [B, C, T]")
+    C, T = centroids.shape[1], table.shape[2]
+    _check_shape(centroids, (B, C, d), "centroids")
+    _need(centroids.dtype == torch.bfloat16 and q_idx.dtype == torch.bfloat16,
+          "the centroid table router takes bfloat16", TypeError)
+    _check_i32(table, (B, C, T), "table")
+    cap = k if cap is None else cap
+    dev = q_idx.device
+    if idx is None:
+        idx = torch.empty((B, 1, cap), dtype=torch.int32, device=dev)
+    if counts is None:
+        counts = torch.empty((B, 1), dtype=torch.int32, device=dev)
+    _check_route_io(B, 1, cap, n_ctx, idx, counts)
+    _check_dev(q_idx, K_idx, centroids, table, n_ctx, idx, counts)
+    ws = _workspace(lib.clsa_csa_route_workspace_size(B, d, n_cap, C, T, P), dev, ws)
+    args = (_ptr(q_idx), _ptr(K_idx), B, d, n_cap, _ptr(n_ctx), _ptr(centroids), _ptr(table), C, T,
+            n_table, P, k, CLSA_BF16, _ptr(idx), _ptr(counts), cap, _ptr(ws), ws.numel(),
+            _stream(stream))
+    return Prepared("clsa_csa_route", lib.clsa_csa_route, args, (idx, counts),
+                    (q_idx, K_idx, centroids, table, n_ctx, idx, counts, ws))
+
+
+def csa_route(q_idx, K_idx, centroids, table, n_table: int, P: int, k: int, **kw):
+    return prepare_csa_route(q_idx, K_idx, centroids, table, n_table, P, k, **kw)()

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libclsa.so")
-SOURCES = ["clsa_api.hip", "clsa_route.hip", "clsa_prefill.hip", "clsa_attn.hip", "clsa_louver.hip"]
+SOURCES = ["clsa_api.hip", "clsa_route.hip", "clsa_prefill.hip", "clsa_attn.hip", "clsa_louver.hip",
+           "clsa_routers.hip"]
 ARCH = os.environ.get("CLSA_OFFLOAD_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -55,6 +55,7 @@ constexpr int kBucketShift = 21;
 constexpr uint32_t kLowMask = (1u << kBucketShift) - 1u;
 constexpr int kMaxChunks = 4096;  // chunks per row
 constexpr int kMaxFilterCH = 2048;  // keys per chunk in filter mode (at most)
+constexpr int kMaxHeads = 64;       // index heads of an aggregated routing call
 
 // what route_score does with the scores
 constexpr int kHist = 0;    // top-k: keys + histogram of the top 11 bits
@@ -86,6 +87,11 @@ struct RouteArgs {
   uint32_t* segcnt;       // [R][C]     candidates found per chunk (true count)
   uint64_t* seg;          // [R][C * segcap] position | score bits << 32, per chunk
   int segcap;             // entries per chunk and row (shared by visible chunks)
+  // cross-layer aggregation (exhaustive path): heads 1 .. H-1 beyond (q, K),
+  // whose scores are added to head 0's before the selection
+  const void* qh[kMaxHeads];
+  const void* Kh[kMaxHeads];
+  int H;
 };
 
 CLSA_DEV int64_t visible(const RouteArgs& a, int r) {
@@ -288,6 +294,22 @@ __global__ __launch_bounds__(kNT) void route_score(RouteArgs a) {
     if (!(pre && it == 0)) issue(wbase);
 #pragma unroll
     for (int u = 0; u < kU; ++u) part[u] = Elem<T>::dot(v[u], qf);
+    if constexpr (TOPK) {
+      // aggregated heads: each head's partial dot products are added before
+      // the lane reduction, so every key sums its heads in the same order
+      for (int h = 1; h < a.H; ++h) {
+        float qhf[kEPL];
+        Elem<T>::load_q(a.qh[h], (size_t)r * D + (size_t)pos * kEPL, qhf);
+        const char* Kbh = static_cast<const char*>(a.Kh[h]) + (size_t)b * a.n_cap * D * sizeof(T);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int64_t j = wbase + u * kKPI + grp;
+          v[u] = load_stream16(Kbh + (size_t)(j < n_vis ? j : 0) * D * sizeof(T) + pos * 16);
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) part[u] += Elem<T>::dot(v[u], qhf);
+      }
+    }
     const float s = reduce_scatter<kU>(part, lane);
     const int64_t j = wbase + pos * kKPI + grp;
     if (MODE == kFilter) {
@@ -949,5 +971,45 @@ extern "C" int clsa_route_threshold(const void* q_idx, const void* K_idx, int B,
   const dim3 grid((unsigned)L.C, (unsigned)R);
   launch_score<kCount>(a, dt, d, grid, s);
   hipLaunchKernelGGL(route_compact<false>, grid, dim3(kNT), 0, s, a);
+  return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
+}
+
+// ------------------------------------------------- cross-layer aggregation
+// clsa_route_aggregated: the exhaustive path with H index heads whose scores
+// are summed per key (see clsa.h).
+extern "C" size_t clsa_route_aggregated_workspace_size(int H, int B, int M, int d, int64_t n_cap,
+                                                       int k, int cap, clsa_dtype dt) {
+  (void)dt;
+  if (H < 1 || H > kMaxHeads || !shape_ok(B, M, d, n_cap, cap) || k < 1) return 0;
+  return make_layout((int64_t)B * M, n_cap, true).total;
+}
+
+extern "C" int clsa_route_aggregated(int H, const void* const* q_idx, const void* const* K_idx,
+                                     int B, int M, int d, int64_t n_cap, const int32_t* n_ctx,
+                                     int64_t q_pos0, int k, clsa_dtype dt, int32_t* idx,
+                                     int32_t* counts, int cap, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (dt != CLSA_F32 && dt != CLSA_BF16) return CLSA_ERR_UNSUPPORTED_DTYPE;
+  if (H < 1 || H > kMaxHeads || !q_idx || !K_idx || !idx || !counts) return CLSA_ERR_INVALID;
+  for (int h = 0; h < H; ++h)
+    if (!q_idx[h] || !K_idx[h]) return CLSA_ERR_INVALID;
+  if (!shape_ok(B, M, d, n_cap, cap) || k < 1 || cap < k) return CLSA_ERR_INVALID;
+  const int64_t R = (int64_t)B * M;
+  const Layout L = make_layout(R, n_cap, true);
+  if (!ws || ws_bytes < L.total) return CLSA_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RouteArgs a = fill_args(L, ws, q_idx[0], K_idx[0], B, M, n_cap, n_ctx, q_pos0, k, nullptr, idx,
+                          counts, cap);
+  a.H = H;
+  for (int h = 0; h < H; ++h) {
+    a.qh[h] = q_idx[h];
+    a.Kh[h] = K_idx[h];
+  }
+  if (zero_fill(ws, L.ctrl_end, s) != hipSuccess) return CLSA_ERR_HIP;
+  const dim3 grid((unsigned)L.C, (unsigned)R);
+  launch_score<kHist>(a, dt, d, grid, s);
+  hipLaunchKernelGGL(route_cands, grid, dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(route_select, dim3((unsigned)R), dim3(kNT), 0, s, a);
+  hipLaunchKernelGGL(route_compact<true>, grid, dim3(kNT), 0, s, a);
   return hipGetLastError() == hipSuccess ? CLSA_OK : CLSA_ERR_HIP;
 }

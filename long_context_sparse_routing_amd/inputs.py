@@ -37,6 +37,7 @@ __all__ = [
     "threshold_counts",
     "torch_dtype",
     "gen_append_rows",
+    "gen_prompt_routing_queries",
 ]
 
 
@@ -283,3 +284,14 @@ def gen_append_rows(wl: Workload, steps: int, device, seed: int | None = None):
     new_k = _randn((steps, wl.L, wl.B, wl.Hkv, wl.D), g, device, dtype=dt)
     new_v = _randn((steps, wl.L, wl.B, wl.Hkv, wl.D), g, device, dtype=dt)
     return new_kidx, new_k, new_v
+
+
+def gen_prompt_routing_queries(wl: Workload, u, M: int, device, seed: int | None = None):
+    """Routing queries of the prompt that preceded a decode workload:
+    [B, M, d], drawn like that workload's decode queries (u_b + 0.3 *
+    N(0,1)/sqrt(d)), so a table built from them at prefill describes the
+    decode steps' queries."""
+    base = wl.base_seed if seed is None else seed
+    g = make_generator(device, seed_of(base, "prompt_q_idx", M))
+    noise = _randn((wl.B, M, wl.d), g, device) / math.sqrt(wl.d)
+    return (u[:, None, :] + 0.3 * noise).to(torch_dtype(wl.dtype)).contiguous()
