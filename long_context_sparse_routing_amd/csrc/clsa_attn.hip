@@ -142,12 +142,6 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine(AttnArgs a) {
 }
 
 // ======================================================= gathered (bf16)
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-CLSA_DEV float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 
 // Sum NV per-lane partials over each group of LANES consecutive lanes,
 // halving the values kept per lane at each butterfly step while more than
@@ -244,21 +238,33 @@ void attn_bf16(AttnArgs a) {
     qw[h] = *reinterpret_cast<const u32x4_t*>(ql + (((size_t)r * a.Hq) + g * G + h) * D + ds * 8);
   __syncthreads();
 
-  // ---- phase A: scores ----
   const int ngroups = (nt + kTPW - 1) / kTPW;
+  // V rows of token slots t < nt with a valid position: bit u of vmask
+  auto load_v = [&](int grp0, u32x4_t (&vv)[kVB], uint32_t& vmask) {
+    vmask = 0u;
+#pragma unroll
+    for (int u = 0; u < kVB; ++u) {
+      const int t = (grp0 + u) * kTPW + tq;
+      const int rw = t < nt ? sidx[t] : -1;
+      vmask |= rw >= 0 ? 1u << u : 0u;
+      vv[u] = load_row16<NT>(Vl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
+    }
+  };
+
+  // ---- phase A: scores ----
   for (int grp0 = w * kAB; grp0 < ngroups; grp0 += kWaves * kAB) {
     u32x4_t kk[kAB];
-    int ts[kAB], rws[kAB];
+    uint32_t kmask = 0u;  // bit u: slot u holds a valid position
 #pragma unroll
     for (int u = 0; u < kAB; ++u) {
       const int t = (grp0 + u) * kTPW + tq;
       const int rw = t < nt ? sidx[t] : -1;
-      ts[u] = t;
-      rws[u] = rw;
+      kmask |= rw >= 0 ? 1u << u : 0u;
       kk[u] = load_row16<NT>(Kl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
     }
 #pragma unroll
     for (int u = 0; u < kAB; ++u) {
+      const int t = (grp0 + u) * kTPW + tq;
       float v[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
@@ -269,10 +275,10 @@ void attn_bf16(AttnArgs a) {
       }
       int base = 0;
       group_reduce<G, kLPT>(v, lane, base);
-      if ((ds & (kShare - 1)) == 0 && ts[u] < nt) {
+      if ((ds & (kShare - 1)) == 0 && t < nt) {
 #pragma unroll
         for (int i = 0; i < kNR; ++i)
-          sc[base + i][ts[u]] = rws[u] >= 0 ? v[i] * a.scale_log2 : -INFINITY;
+          sc[base + i][t] = (kmask >> u) & 1u ? v[i] * a.scale_log2 : -INFINITY;
       }
     }
   }
@@ -280,20 +286,10 @@ void attn_bf16(AttnArgs a) {
   // softmax rather than after it.  The barriers around the softmax publish
   // LDS only (scores, then probabilities), so they leave these loads in
   // flight.
-  auto load_v = [&](int grp0, u32x4_t (&vv)[kVB], int (&ts)[kVB], int (&rws)[kVB]) {
-#pragma unroll
-    for (int u = 0; u < kVB; ++u) {
-      const int t = (grp0 + u) * kTPW + tq;
-      const int rw = t < nt ? sidx[t] : -1;
-      ts[u] = t;
-      rws[u] = rw;
-      vv[u] = load_row16<NT>(Vl + (head_base + (size_t)(rw < 0 ? 0 : rw) * a.Hkv) * D + ds * 8);
-    }
-  };
   u32x4_t vv0[kVB];
-  int ts0[kVB], rws0[kVB];
+  uint32_t vmask0 = 0u;
   const bool first_v = w * kVB < ngroups;  // wave-uniform
-  if (first_v) load_v(w * kVB, vv0, ts0, rws0);
+  if (first_v) load_v(w * kVB, vv0, vmask0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   // ---- phase B: softmax per head over the split; wave w owns heads
@@ -326,9 +322,10 @@ void attn_bf16(AttnArgs a) {
   for (int h = 0; h < G; ++h)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
-  auto fold_v = [&](const u32x4_t (&vv)[kVB], const int (&ts)[kVB], const int (&rws)[kVB]) {
+  auto fold_v = [&](int grp0, const u32x4_t (&vv)[kVB], uint32_t vmask) {
 #pragma unroll
     for (int u = 0; u < kVB; ++u) {
+      const int t = (grp0 + u) * kTPW + tq;
       float vf[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -337,18 +334,18 @@ void attn_bf16(AttnArgs a) {
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = rws[u] >= 0 ? sc[h][ts[u]] : 0.f;
+        const float p = (vmask >> u) & 1u ? sc[h][t] : 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[h][e] = fmaf(p, vf[e], acc[h][e]);
       }
     }
   };
-  if (first_v) fold_v(vv0, ts0, rws0);
+  if (first_v) fold_v(w * kVB, vv0, vmask0);
   for (int grp0 = w * kVB + kWaves * kVB; grp0 < ngroups; grp0 += kWaves * kVB) {
     u32x4_t vv[kVB];
-    int ts[kVB], rws[kVB];
-    load_v(grp0, vv, ts, rws);
-    fold_v(vv, ts, rws);
+    uint32_t vmask;
+    load_v(grp0, vv, vmask);
+    fold_v(grp0, vv, vmask);
   }
   // sum the token slots sharing a dim slice, then the 4 waves (in LDS)
 #pragma unroll
@@ -554,7 +551,10 @@ void launch_fast_gna(int D, dim3 grid, dim3 block, hipStream_t s, const AttnArgs
 // few load rounds are latency-bound: 16 single-layer decode launches 367 ->
 // 345 us) or rows share positions (cached loads); 2 for long streaming
 // splits, whose loads already keep HBM busy (the 16-layer decode launch is
-// 1 % slower with 4).
+// 1 % slower with 4).  Issuing a short split's V rows together with its K
+// rows (8 K + 4 V per lane) shortened each workgroup by 1 us but not the
+// launch (16 single-layer launches 340 us either way; one sequence's
+// 16-layer launch 28.3 -> 30.1 us).
 template <int G>
 void launch_fast_g(int D, bool nt, bool short_split, dim3 grid, dim3 block, hipStream_t s,
                    const AttnArgs& a) {

@@ -33,6 +33,14 @@ CLSA_DEV uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// c + a.lo * b.lo + a.hi * b.hi over two packed bf16 pairs (v_dot2_f32_bf16)
+CLSA_DEV float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // ------------------------------------------------------- order-preserving key
 // Monotone map float -> uint32: a > b  <=>  key(a) > key(b), and -0.0 maps to
 // the key of +0.0 so the two compare equal (as they do as floats).

@@ -306,9 +306,12 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
 
 // Rows whose keys no other row shares (a decode step: one query per
 // sequence), sampled as row_plan says: ceil(ns / kNT) workgroups score the
-// samples on the matrix cores (one per thread) and store their 16-bit key
-// prefixes -- each wave's kRowTop largest when the plan is compact, else
-// all of them -- for the score pass, which ranks them (rank_row_samples).
+// samples, one per thread, on the VALU (v_dot2_f32_bf16 against the row's
+// query; a single query row has no matrix shape to give the matrix cores),
+// and store their 16-bit key prefixes -- each wave's kRowTop largest when
+// the plan is compact, else all of them -- for the score pass, which ranks
+// them (rank_row_samples).  The sample scores only set a threshold that the
+// select checks, so their summation order does not matter.
 constexpr int kRowNs = kRowSamples;
 constexpr int kRowSampleWG = kRowNs / kNT;  // one sample per thread
 
@@ -320,63 +323,39 @@ __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
   const int64_t k_eff = a.k < n_vis ? a.k : n_vis;
   if (k_eff >= n_vis) return;  // the select takes every visible key
   const RowPlan p = row_plan(n_vis, k_eff);
-  const int s0 = blockIdx.x * kNT + w * kWave;  // the wave's 64 samples: 4 MFMA tiles
+  const int s0 = blockIdx.x * kNT + w * kWave;  // the wave's 64 samples, one per lane
   if (p.rho > p.ns || s0 >= p.ns) return;
   uint16_t* row = samp + (size_t)r * kRowNs;
 
-  // A operand: the row's query in all 16 MFMA rows; B: 16 sampled keys, so
-  // lanes 0..15 receive the scores of their samples in accumulator value 0
-  bf16x8_t qa[D / 32], kb[4][D / 32];
+  const int smp = s0 + lane;
+  u32x4_t kv[D / 8];
+  const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(
+      a.K + ((size_t)b * a.n_cap + (size_t)((int64_t)(smp < p.ns ? smp : 0) * n_vis / p.ns)) * D);
 #pragma unroll
-  for (int st = 0; st < D / 32; ++st)
-    qa[st] = __builtin_bit_cast(
-        bf16x8_t, *reinterpret_cast<const u32x4_t*>(a.q + (size_t)r * D + 32 * st + 8 * (lane / 16)));
+  for (int st = 0; st < D / 8; ++st) kv[st] = kp[st];
+  const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + (size_t)r * D);
+  float acc = 0.f;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int smp = s0 + u * 16 + lane % 16;
-#pragma unroll
-    for (int st = 0; st < D / 32; ++st) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (smp < p.ns)
-        v = *reinterpret_cast<const u32x4_t*>(
-            a.K + ((size_t)b * a.n_cap + (size_t)((int64_t)smp * n_vis / p.ns)) * D + 32 * st +
-            8 * (lane / 16));
-      kb[u][st] = __builtin_bit_cast(bf16x8_t, v);
-    }
+  for (int st = 0; st < D / 8; ++st) {
+    const u32x4_t qv = qp[st];
+    acc = dot2(kv[st][0], qv[0], acc);
+    acc = dot2(kv[st][1], qv[1], acc);
+    acc = dot2(kv[st][2], qv[2], acc);
+    acc = dot2(kv[st][3], qv[3], acc);
   }
-  // lane l < 16 holds samples s0 + 16 u + l; samples past ns count as 0,
-  // below every real prefix
-  uint32_t key[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < D / 32; ++st)
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[st], kb[u][st], c, 0, 0, 0);
-    const int smp = s0 + u * 16 + lane;
-    key[u] = (lane < 16 && smp < p.ns) ? score_key(c[0]) >> 16 : 0u;
-  }
+  // samples past ns count as 0, below every real prefix
+  uint32_t key = smp < p.ns ? score_key(acc) >> 16 : 0u;
   if (p.compact) {
     // the wave's kRowTop largest: take the maximum, knock one copy out
 #pragma unroll
     for (int t = 0; t < kRowTop; ++t) {
-      uint32_t mx = key[0];
-#pragma unroll
-      for (int u = 1; u < 4; ++u) mx = key[u] > mx ? key[u] : mx;
-      mx = wave_max_u32(mx);
-      const uint64_t has = __ballot(key[0] == mx || key[1] == mx || key[2] == mx || key[3] == mx);
-      if (lane == __ffsll((unsigned long long)has) - 1) {
-        bool gone = false;
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (!gone && key[u] == mx) key[u] = 0u, gone = true;
-      }
+      const uint32_t mx = wave_max_u32(key);
+      const uint64_t has = __ballot(key == mx);
+      if (lane == __ffsll((unsigned long long)has) - 1) key = 0u;
       if (lane == 0) row[(s0 / kWave) * kRowTop + t] = (uint16_t)mx;
     }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (lane < 16 && s0 + u * 16 + lane < p.ns) row[s0 + u * 16 + lane] = (uint16_t)key[u];
+  } else if (smp < p.ns) {
+    row[smp] = (uint16_t)key;
   }
 }
 
