@@ -175,10 +175,11 @@ CLSA_DEV uint32_t row_seg_cap(int C, int segcap, int CH, int64_t cv) {
   return (uint32_t)(c < CH ? c : CH);
 }
 
-// Samples per row of the decode-row threshold estimate (at most), and how
-// many of each 64 consecutive samples' largest key prefixes are kept.
+// Samples per row of the decode-row threshold estimate (at most), and at
+// most how many of each 64 consecutive samples' largest key prefixes are
+// kept.
 constexpr int kRowSamples = 4096;
-constexpr int kRowTop = 8;
+constexpr int kRowTop = 16;
 
 // rho-th largest 16-bit key among those held by one wave, exactly: entry u
 // of v[] counts where valid(u) holds in its lane (rho at most their number).
@@ -253,18 +254,22 @@ CLSA_DEV uint32_t wave_kth_u16(const uint32_t (&v)[NPL], Valid valid, uint32_t r
 
 // Sampling plan of a decode row (one query whose keys no other row shares):
 // ns = min(n_vis, kRowSamples) samples, sample i at floor(i n_vis / ns);
-// rho from sample_rank; and whether only the kRowTop largest key prefixes
-// of each 64 consecutive samples are kept (compact: rho well inside their
-// number) or every sample.
+// rho from sample_rank; and whether only the top = 8 (or 16, when rho needs
+// them) largest key prefixes of each 64 consecutive samples are kept
+// (compact: rho well inside their number) or every sample.  Ranking every
+// sample takes one wave 8 us at 32K keys (4096 LDS atomics into a
+// histogram whose middle bins collide), 16 per 64 samples about 1 us.
 struct RowPlan {
-  int ns, rho, nkept;
+  int ns, rho, top, nkept;
   bool compact;
 };
 CLSA_DEV RowPlan row_plan(int64_t n_vis, int64_t k_eff) {
   RowPlan p;
   p.ns = (int)(n_vis < kRowSamples ? n_vis : kRowSamples);
   p.rho = sample_rank(n_vis, k_eff, p.ns);
-  p.nkept = (p.ns + kWave - 1) / kWave * kRowTop;
+  const int waves = (p.ns + kWave - 1) / kWave;
+  p.top = 2 * p.rho <= waves * 8 ? 8 : kRowTop;
+  p.nkept = waves * p.top;
   p.compact = 2 * p.rho <= p.nkept;
   return p;
 }
@@ -275,19 +280,27 @@ CLSA_DEV RowPlan row_plan(int64_t n_vis, int64_t k_eff) {
 // rho-th largest sample (the kept prefixes are some of the samples), so it
 // is a lower bound of the sample's rho-th score either way.  h: 1024 words
 // of LDS for this wave.
-// compact lists: lane l holds kept entries 8 l .. 8 l + 7 (zeros past the list)
+// compact lists: lane l holds wave l's kept entries top l .. top l + top - 1
+// in v[0 .. top) (zeros past the list)
 CLSA_DEV void load_row_kept(const uint16_t* row, const RowPlan& p, uint32_t (&v)[kRowTop]) {
-  static_assert(kRowTop == 8, "one 16-byte load per lane");
+  static_assert(kRowTop == 16, "at most two 16-byte loads per lane");
   const int lane = lane_id();
-  const int last = p.nkept / kRowTop - 1;  // lanes past the list re-read its last entries
-  const u32x4_t x = reinterpret_cast<const u32x4_t*>(row)[lane < last ? lane : last];
+  const int last = p.nkept / p.top - 1;  // lanes past the list re-read its last entries
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(row + (lane < last ? lane : last) * p.top);
+  const u32x4_t x0 = src[0];
+  const u32x4_t x1 = src[p.top / 8 - 1];  // the same 16 bytes again when top = 8
   const bool ok = lane <= last;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = ok ? (x[e / 2] >> (16 * (e & 1))) & 0xffffu : 0u;
+  for (int e = 0; e < 8; ++e) {
+    v[e] = ok ? (x0[e / 2] >> (16 * (e & 1))) & 0xffffu : 0u;
+    v[8 + e] = ok && p.top > 8 ? (x1[e / 2] >> (16 * (e & 1))) & 0xffffu : 0u;
+  }
 }
 CLSA_DEV float rank_row_kept(const uint32_t (&v)[kRowTop], const RowPlan& p, uint32_t* h) {
-  const bool ok = kRowTop * lane_id() < p.nkept;
-  return key_to_float(wave_kth_u16(v, [&](int) { return ok; }, (uint32_t)p.rho, h) << 16);
+  const bool ok = p.top * lane_id() < p.nkept;
+  const int top = p.top;
+  return key_to_float(
+      wave_kth_u16(v, [&](int u) { return ok && u < top; }, (uint32_t)p.rho, h) << 16);
 }
 
 CLSA_DEV float rank_row_samples(const uint16_t* row, const RowPlan& p, uint32_t* h) {

@@ -308,7 +308,7 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
 // sequence), sampled as row_plan says: ceil(ns / kNT) workgroups score the
 // samples, one per thread, on the VALU (v_dot2_f32_bf16 against the row's
 // query; a single query row has no matrix shape to give the matrix cores),
-// and store their 16-bit key prefixes -- each wave's kRowTop largest when
+// and store their 16-bit key prefixes -- each wave's p.top largest when
 // the plan is compact, else all of them -- for the score pass, which ranks
 // them (rank_row_samples).  The sample scores only set a threshold that the
 // select checks, so their summation order does not matter.
@@ -346,13 +346,12 @@ __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
   // samples past ns count as 0, below every real prefix
   uint32_t key = smp < p.ns ? score_key(acc) >> 16 : 0u;
   if (p.compact) {
-    // the wave's kRowTop largest: take the maximum, knock one copy out
-#pragma unroll
-    for (int t = 0; t < kRowTop; ++t) {
+    // the wave's p.top largest: take the maximum, knock one copy out
+    for (int t = 0; t < p.top; ++t) {
       const uint32_t mx = wave_max_u32(key);
       const uint64_t has = __ballot(key == mx);
       if (lane == __ffsll((unsigned long long)has) - 1) key = 0u;
-      if (lane == 0) row[(s0 / kWave) * kRowTop + t] = (uint16_t)mx;
+      if (lane == 0) row[(s0 / kWave) * p.top + t] = (uint16_t)mx;
     }
   } else if (smp < p.ns) {
     row[smp] = (uint16_t)key;
