@@ -28,6 +28,7 @@
 // All keys of a row are ranked on values computed the same way, so equal key
 // rows score exactly equal and the lower position wins.
 #include "clsa_common.h"
+#include "clsa_rowplan.h"
 #include "clsa_select.h"
 
 namespace clsa {

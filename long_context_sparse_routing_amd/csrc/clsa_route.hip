@@ -44,6 +44,7 @@
 #include <mutex>
 
 #include "clsa_common.h"
+#include "clsa_rowplan.h"
 
 namespace clsa {
 
