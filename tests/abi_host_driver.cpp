@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <initializer_list>
 
 #include "clsa.h"
 
@@ -200,6 +201,73 @@ void append_rejects() {
                         nullptr) == CLSA_ERR_INVALID);
 }
 
+void router_paths() {
+  const int32_t* fi = static_cast<const int32_t*>(kFake);
+  int32_t* o = static_cast<int32_t*>(kFake);
+  const size_t big = size_t{1} << 40;
+  // aggregated routing: sizes over head counts and shapes, then rejects
+  const int Hs[] = {-1, 0, 1, 16, 64, 65, 1 << 20};
+  for (int H : Hs)
+    for (int64_t n : {int64_t{1}, int64_t{131072}, int64_t{524289}, int64_t{1} << 40}) {
+      const size_t w = clsa_route_aggregated_workspace_size(H, 8, 1, 64, n, 2048, 2048, CLSA_BF16);
+      EXPECT((w == 0) == (H < 1 || H > 64 || !route_shape_valid(8, 1, 64, n, 2048)));
+    }
+  const void* hp[64];
+  for (int h = 0; h < 64; ++h) hp[h] = kFake;
+  EXPECT(clsa_route_aggregated(0, hp, hp, 2, 1, 64, 4096, nullptr, -1, 64, CLSA_BF16, o, o, 64,
+                               kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_route_aggregated(65, hp, hp, 2, 1, 64, 4096, nullptr, -1, 64, CLSA_BF16, o, o, 64,
+                               kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_route_aggregated(2, nullptr, hp, 2, 1, 64, 4096, nullptr, -1, 64, CLSA_BF16, o, o,
+                               64, kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_route_aggregated(2, hp, hp, 2, 1, 64, 4096, nullptr, -1, 64,
+                               static_cast<clsa_dtype>(4), o, o, 64, kFake, big, nullptr) ==
+         CLSA_ERR_UNSUPPORTED_DTYPE);
+  EXPECT(clsa_route_aggregated(2, hp, hp, 2, 1, 64, 4096, nullptr, -1, 64, CLSA_BF16, o, o, 64,
+                               nullptr, 0, nullptr) == CLSA_ERR_WORKSPACE);
+  // centroid table: sizes up to and past every limit
+  const int Cs[] = {-1, 0, 1, 64, 256, 512, 1024, 1025, 1 << 20};
+  const int Ts[] = {-1, 0, 1, 2048, 2049};
+  const int ds[] = {16, 32, 64, 128};
+  for (int C : Cs)
+    for (int T : Ts)
+      for (int d : ds) {
+        const bool ok = C >= 1 && C <= 1024 && T >= 1 && T <= 2048 &&
+                        (d == 32 || d == 64 || d == 128) && int64_t{C} * d * 4 <= 65536;
+        const size_t wb = clsa_csa_build_workspace_size(8, 4096, d, 131072, C, T);
+        EXPECT((wb > 0) == (ok && C <= 4096));
+        for (int P : {0, 1, 3, 16, 17}) {
+          const size_t wr = clsa_csa_route_workspace_size(8, d, 131072, C, T, P);
+          EXPECT((wr > 0) == (ok && P >= 1 && P <= 16 && P <= C));
+        }
+      }
+  EXPECT(clsa_csa_build_workspace_size(1 << 20, 1 << 20, 64, 131072, 64, 256) == 0);
+  EXPECT(clsa_csa_build(kFake, kFake, 2, 256, 64, 4096, nullptr, 16, 4, 256, CLSA_F32, kFake, o,
+                        kFake, big, nullptr) == CLSA_ERR_UNSUPPORTED_DTYPE);
+  EXPECT(clsa_csa_build(kFake, kFake, 5000, 256, 64, 4096, nullptr, 16, 4, 256, CLSA_BF16, kFake,
+                        o, kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_csa_build(kFake, kFake, 2, 256, 64, 4096, nullptr, 16, 101, 256, CLSA_BF16, kFake,
+                        o, kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_csa_build(kFake, kFake, 2, 256, 64, 4096, nullptr, 16, 4, 256, CLSA_BF16, kFake, o,
+                        kFake, 16, nullptr) == CLSA_ERR_WORKSPACE);
+  EXPECT(clsa_csa_route(kFake, kFake, 2, 64, int64_t{1} << 40, nullptr, kFake, fi, 16, 256, 0, 4,
+                        64, CLSA_BF16, o, o, 64, kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_csa_route(kFake, kFake, 2, 64, 8192, nullptr, kFake, fi, 16, 256, 1000, 4, 64,
+                        CLSA_BF16, o, o, 64, kFake, big, nullptr) == CLSA_ERR_INVALID);
+  EXPECT(clsa_csa_route(kFake, kFake, 2, 64, 4096, nullptr, kFake, fi, 16, 256, 4000, 4, 64,
+                        CLSA_BF16, o, o, 64, kFake, 8, nullptr) == CLSA_ERR_WORKSPACE);
+  // Louver index: sizes over extreme shapes (no overflow, zero when refused)
+  for (int64_t n : {int64_t{-1}, int64_t{0}, int64_t{1}, int64_t{131072}, int64_t{1} << 24,
+                    (int64_t{1} << 24) + 1, int64_t{1} << 40})
+    for (int S : {0, 1, 2, 3, 4, 8})
+      for (int r : {0, 8, 64, 256, 257}) {
+        const size_t ib = clsa_louver_index_bytes(16, 128, n, S, r);
+        const size_t wb = clsa_louver_build_workspace_size(16, 128, n, S, r);
+        EXPECT((ib == 0) == (wb == 0));
+        if (n < 1 || n > (int64_t{1} << 24)) EXPECT(ib == 0);
+      }
+}
+
 void strings() {
   for (int s = -1000; s <= 1000; ++s) {
     const char* t = clsa_status_string(s);
@@ -216,6 +284,7 @@ int main() {
   route_rejects();
   attn_rejects();
   append_rejects();
+  router_paths();
   strings();
   if (g_fail) {
     std::fprintf(stderr, "%d expectations failed\n", g_fail);

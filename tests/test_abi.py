@@ -250,3 +250,89 @@ def _lv_query(lib, q=FAKE, K=FAKE, B=2, d=64, n_cap=9000, tau=FAKE, dt=BF16, S=1
 ])
 def test_louver_query_rejects(lib, kw, want):
     assert _lv_query(lib, **kw) == want
+
+
+# ------------------------------------------------------ alternative routers
+def _ptrs(*p):
+    return (ctypes.c_void_p * len(p))(*p)
+
+
+def test_aggregated_workspace_sizes(lib):
+    f = lib.clsa_route_aggregated_workspace_size
+    one = f(1, 8, 1, 64, 131072, 2048, 2048, BF16)
+    assert one > 0 and f(16, 8, 1, 64, 131072, 2048, 2048, BF16) == one  # heads add no workspace
+    for bad in ((0, 8, 1, 64, 4096, 64, 64, BF16), (65, 8, 1, 64, 4096, 64, 64, BF16),
+                (2, 8, 1, 48, 4096, 64, 64, BF16), (2, 8, 1, 64, 4096, 0, 64, BF16)):
+        assert f(*bad) == 0, bad
+
+
+def _agg(lib, H=2, q=None, K=None, B=2, M=1, d=64, n_cap=4096, k=64, dt=BF16, idx=FAKE,
+         counts=FAKE, cap=64, ws=FAKE, ws_bytes=1 << 40):
+    q = _ptrs(*([FAKE] * H)) if q is None else q
+    K = _ptrs(*([FAKE] * H)) if K is None else K
+    return lib.clsa_route_aggregated(H, q, K, B, M, d, n_cap, NULL, -1, k, dt, idx, counts, cap,
+                                     ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(H=0), INVALID), (dict(H=65), INVALID), (dict(q=NULL), INVALID), (dict(K=NULL), INVALID),
+    (dict(q=_ptrs(FAKE, NULL)), INVALID), (dict(K=_ptrs(NULL, FAKE)), INVALID),
+    (dict(dt=7), DTYPE), (dict(idx=NULL), INVALID), (dict(cap=32), INVALID), (dict(k=0), INVALID),
+    (dict(d=48), INVALID), (dict(ws=NULL), WORKSPACE), (dict(ws_bytes=64), WORKSPACE),
+])
+def test_aggregated_rejects(lib, kw, want):
+    assert _agg(lib, **kw) == want
+
+
+def test_centroid_table_workspace_sizes(lib):
+    b = lib.clsa_csa_build_workspace_size
+    assert b(8, 4096, 64, 131072, 64, 2048) > 0
+    for bad in ((8, 32, 64, 131072, 64, 2048),      # fewer queries than centroids
+                (8, 4096, 64, 131072, 1025, 2048),  # too many centroids
+                (8, 4096, 128, 131072, 256, 2048),  # centroids do not fit the LDS (C d > 16384)
+                (8, 4096, 64, 131072, 64, 2049), (8, 4096, 64, 131072, 64, 0),
+                (8, 4096, 48, 131072, 64, 256), (8, 4096, 64, 524289, 64, 256)):
+        assert b(*bad) == 0, bad
+    r = lib.clsa_csa_route_workspace_size
+    assert r(8, 64, 131072, 64, 2048, 3) > 0
+    for bad in ((8, 64, 131072, 64, 2048, 0), (8, 64, 131072, 64, 2048, 17),
+                (8, 64, 131072, 2, 2048, 3)):  # more probes than centroids
+        assert r(*bad) == 0, bad
+
+
+def _csa_build(lib, q=FAKE, K=FAKE, B=2, M=256, d=64, n_cap=4096, C=16, rounds=4, T=256, dt=BF16,
+               cent=FAKE, table=FAKE, ws=FAKE, ws_bytes=1 << 40):
+    return lib.clsa_csa_build(q, K, B, M, d, n_cap, NULL, C, rounds, T, dt, cent, table, ws,
+                              ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=F32), DTYPE), (dict(q=NULL), INVALID), (dict(K=NULL), INVALID),
+    (dict(cent=NULL), INVALID), (dict(table=NULL), INVALID), (dict(M=8), INVALID),
+    (dict(C=0), INVALID), (dict(T=2049), INVALID), (dict(rounds=101), INVALID),
+    (dict(rounds=-1), INVALID), (dict(B=5000, C=16), INVALID),  # B C > 65535
+    (dict(ws=NULL), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE),
+])
+def test_centroid_table_build_rejects(lib, kw, want):
+    assert _csa_build(lib, **kw) == want
+
+
+def _csa_route(lib, q=FAKE, K=FAKE, B=2, d=64, n_cap=4096, cent=FAKE, table=FAKE, C=16, T=256,
+               n_table=4000, P=4, k=64, dt=BF16, idx=FAKE, counts=FAKE, cap=64, ws=FAKE,
+               ws_bytes=1 << 40):
+    return lib.clsa_csa_route(q, K, B, d, n_cap, NULL, cent, table, C, T, n_table, P, k, dt, idx,
+                              counts, cap, ws, ws_bytes, NULL)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(dt=F32), DTYPE), (dict(q=NULL), INVALID), (dict(cent=NULL), INVALID),
+    (dict(table=NULL), INVALID), (dict(idx=NULL), INVALID), (dict(counts=NULL), INVALID),
+    (dict(P=0), INVALID), (dict(P=17, C=32), INVALID), (dict(P=5, C=4), INVALID),
+    (dict(k=0), INVALID), (dict(cap=32), INVALID), (dict(n_table=5000), INVALID),
+    (dict(n_table=-1), INVALID),
+    (dict(P=16, T=512, C=32), INVALID),  # 16 x 512 candidates + a buffer of 96 > 8192
+    (dict(n_cap=8192, n_table=1000), INVALID),  # a buffer of 7192 + 4 x 256 > 8192
+    (dict(ws=NULL), WORKSPACE), (dict(ws_bytes=1024), WORKSPACE),
+])
+def test_centroid_table_route_rejects(lib, kw, want):
+    assert _csa_route(lib, **kw) == want
