@@ -258,7 +258,6 @@ __global__ __launch_bounds__(kSelNT) void csa_select(CsaArgs a) {
   __shared__ SelScratch S;
   __shared__ uint32_t tot;
   const int b = blockIdx.x, tid = threadIdx.x;
-  const int64_t n_vis = csa_visible(a, b);
   const int wpt = (int)((ceil_div64(ceil_div64(a.n_cap, 32), kSelNT) + 3) / 4 * 4);
   const int w0 = tid * wpt;
   for (int i = w0; i < w0 + wpt; i += 4) bitmap4[i / 4] = u32x4_t{0u, 0u, 0u, 0u};
@@ -300,7 +299,6 @@ __global__ __launch_bounds__(kSelNT) void csa_select(CsaArgs a) {
   __syncthreads();
   for (int i = w0; i < w0 + wpt; i += 4) bitmap4[i / 4] = u32x4_t{0u, 0u, 0u, 0u};
   __syncthreads();
-  (void)n_vis;
   select_emit<kCsaPerT>(key, pos, kCsaPerT, k_eff, S, bitmap4, wpt, out);
 }
 
