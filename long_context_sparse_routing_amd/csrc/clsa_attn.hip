@@ -4,9 +4,10 @@
 // cross-decoder layer runs softmax attention over the same routed KV
 // positions, produced once per query token.
 //
-// Grid: (split, row, layer).  A split is TS consecutive entries of the row's
-// index list; its workgroup writes either the final output (one split) or
-// a partial (m, l, acc) that attn_combine merges with the log-sum-exp rule.
+// Grid: (split, row, layer).  A row's index list is cut into ceil(count / TS)
+// splits of near-equal length; a split's workgroup writes either the final
+// output (one split) or a partial (m, l, acc) that attn_combine merges with
+// the log-sum-exp rule.
 // No workgroup waits for another; the kernel boundary orders the merge.
 //
 // attn_bf16  (bf16, D = 64/128/256, Hq/Hkv in {1,2,4,8,16}): one workgroup per
@@ -53,6 +54,13 @@ CLSA_DEV int row_count(const AttnArgs& a, int r) {
 CLSA_DEV int row_splits(const AttnArgs& a, int cnt) {
   const int s = (cnt + a.TS - 1) / a.TS;
   return s < 1 ? 1 : s;
+}
+// Entries [begin, end) of split s of a row's cnt entries: the row's nsplit
+// splits are as equal as integers allow (each at most TS), so that no
+// split of a long row is a short remainder.
+CLSA_DEV void split_range(int cnt, int nsplit, int s, int& begin, int& end) {
+  begin = (int)(((int64_t)s * cnt) / nsplit);
+  end = (int)(((int64_t)(s + 1) * cnt) / nsplit);
 }
 
 template <typename T> CLSA_DEV T from_f32(float x);
@@ -215,9 +223,9 @@ void attn_bf16(AttnArgs a) {
   const int cnt = row_count(a, r);
   const int nsplit = row_splits(a, cnt);
   if (s >= nsplit) return;
-  const int t_begin = s * a.TS;
-  int nt = cnt - t_begin;
-  nt = nt < a.TS ? nt : a.TS;  // tokens of this split, <= kTS
+  int t_begin, t_stop;
+  split_range(cnt, nsplit, s, t_begin, t_stop);
+  const int nt = t_stop - t_begin;  // tokens of this split, <= TS <= kTS
 
   const int b = r / a.M;
   const uint16_t* Kl = static_cast<const uint16_t*>(a.K[l]);
@@ -396,9 +404,8 @@ __global__ __launch_bounds__(256) void attn_generic(AttnArgs a) {
   const int cnt = row_count(a, r);
   const int nsplit = row_splits(a, cnt);
   if (s >= nsplit) return;
-  const int t_begin = s * a.TS;
-  int t_end = t_begin + a.TS;
-  t_end = t_end < cnt ? t_end : cnt;
+  int t_begin, t_end;
+  split_range(cnt, nsplit, s, t_begin, t_end);
   const int b = r / a.M;
   const int Hq = a.Hq, D = a.D, G = a.Hq / a.Hkv;
   const int pairs = Hq * D;
@@ -519,13 +526,14 @@ Plan make_plan(int L, int B, int M, int Hq, int Hkv, int D, int cap, clsa_dtype 
   TS = (TS + kTB - 1) / kTB * kTB;
   // Lists longer than a top-k budget (threshold selection) differ in length
   // from row to row: shorter splits spread the long ones over more
-  // workgroups (threshold lists of up to 8192 at 128K: 721 -> 616 us per
-  // 16-layer call with 512-key splits), but no more than 16 per row, so
-  // that very long uniform lists (dense attention) keep few, long splits.
+  // workgroups (threshold lists of 256 .. 8192 at 128K, 16 layers: 721 us
+  // per call unsplit, 471 us with splits of at most 512, 457 us with 768),
+  // but no more than 11 per row.  Splits of 1024 measured 487 us: the
+  // longest rows' workgroups then form a long tail.
   if (p.fast && cap > 2048) {
-    int64_t lim = (cap + 15) / 16;
+    int64_t lim = (cap + 10) / 11;
     lim = (lim + kTB - 1) / kTB * kTB;
-    if (lim < 512) lim = 512;
+    if (lim < 768) lim = 768;
     if (TS > lim) TS = lim;
   }
   p.TS = (int)TS;
