@@ -38,14 +38,20 @@ struct AppendArgs {
 // blockIdx.x = tensor (K0, V0, K1, V1, ..., then the routing keys), y = sequence
 __global__ __launch_bounds__(128) void kv_append_kernel(AppendArgs a) {
   const int t = blockIdx.x, b = blockIdx.y;
-  const int p = a.pos[b];
-  if (p < 0 || (int64_t)p >= a.n_cap) return;
   const int rb = t < a.n_kv ? a.row_bytes_kv : a.row_bytes_idx;
+  const int nv = rb / 16;
   const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(a.src[t]) +
                                                     (size_t)b * rb);
+  // the row's first 16-byte pieces are requested together with the slot, so
+  // the copy waits on memory once
+  const bool first = (int)threadIdx.x < nv;
+  const uint4 v0 = first ? src[threadIdx.x] : uint4{};
+  const int p = a.pos[b];
+  if (p < 0 || (int64_t)p >= a.n_cap) return;
   uint4* dst = reinterpret_cast<uint4*>(static_cast<char*>(a.dst[t]) +
                                         ((size_t)b * a.n_cap + p) * rb);
-  for (int i = threadIdx.x; i < rb / 16; i += blockDim.x) dst[i] = src[i];
+  if (first) dst[threadIdx.x] = v0;
+  for (int i = threadIdx.x + blockDim.x; i < nv; i += blockDim.x) dst[i] = src[i];
 }
 
 }  // namespace clsa
