@@ -160,3 +160,44 @@ def test_centroid_table_decode_workload():
           f"{[round(r, 3) for r in recall]} (diagnostic)", flush=True)
     del K_idx
     torch.cuda.empty_cache()
+
+
+def test_router_edge_cases():
+    """Degenerate sizes: a lookup whose candidates are fewer than k (every
+    candidate returned, count = candidates), a build with no k-means round
+    (centroids are the starting queries), aggregated routing with k at or
+    above the visible keys and a sequence with no visible key."""
+    g = _g(790)
+    B, M, n, d, C, T = 2, 128, 3000, 32, 8, 40
+    q = _clustered_queries(B, M, d, C, 791)
+    K = torch.randn((B, n, d), generator=g).to(torch.bfloat16)
+    cent, table = clsa.csa_build(q.to(DEV), K.to(DEV), C, T, rounds=0)
+    torch.cuda.synchronize()
+    first = q[:, [(c * M) // C for c in range(C)]]  # rounds = 0: the starting queries
+    assert torch.equal(cent.cpu(), first)
+    qd = q[:, :1].contiguous()
+    idx, counts = clsa.csa_route(qd.to(DEV), K.to(DEV), cent, table, n, 1, 100, cap=110)
+    torch.cuda.synchronize()
+    gcent, gtab = f64(cent), table.cpu().numpy()
+    rows = []
+    for b in range(B):
+        sel, cand, s_all = RO.table_route(f64(qd)[b, 0], f64(K[b]), gcent[b], gtab[b], n, n, 1,
+                                          100)
+        assert len(sel) == T and counts[b, 0].item() == T  # every candidate, fewer than k
+        s = np.full(n, -np.inf)
+        s[cand] = s_all[cand]
+        rows.append((b, sel, s))
+    _check_rows(idx.cpu().numpy(), counts.cpu().numpy(), 110, rows)
+    # aggregated: k above the visible keys, and a sequence with none
+    H = 3
+    Ka = torch.randn((H, 3, 500, 64), generator=g).to(torch.bfloat16)
+    qa = (torch.randn((H, 3, 1, 64), generator=g) / 8).to(torch.bfloat16)
+    nc = torch.tensor([500, 37, 0], dtype=torch.int32, device=DEV)
+    ia, ca = clsa.route_aggregated(qa.to(DEV), Ka.to(DEV), 64, n_ctx=nc, cap=64)
+    torch.cuda.synchronize()
+    assert ca[:, 0].cpu().tolist() == [64, 37, 0]
+    assert ia[1, 0, :37].cpu().tolist() == list(range(37)) and bool((ia[1, 0, 37:] == -1).all())
+    assert bool((ia[2, 0] == -1).all())
+    sel, s = RO.aggregated_route([f64(qa[h, 0, 0]) for h in range(H)],
+                                 [f64(Ka[h, 0]) for h in range(H)], 500, 64)
+    _check_rows(ia.cpu().numpy(), ca.cpu().numpy(), 64, [(0, sel, s)])
