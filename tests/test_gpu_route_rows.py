@@ -114,3 +114,26 @@ def test_many_sequences_take_the_longest_chunks():
     torch.cuda.synchronize()
     for b in (0, 3, 4, 13, 31):  # one sequence at a time: the host copy stays small
         _check(idx[b:b + 1], counts[b:b + 1], q[b:b + 1], K[b:b + 1], [n_ctx[b]], -1, 2048, 2048)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_empty_and_tiny_contexts(dtype):
+    # contexts of 0 and 1 keys, one below, at and above k, and a long one,
+    # in one call (the sampled path for bf16, the exhaustive one for fp32);
+    # then k = 1
+    g = _gen(950)
+    n = 50000
+    n_ctx = [0, 1, 2047, 2048, 2049, n]
+    B = len(n_ctx)
+    K = torch.randn((B, n, 64), generator=g).to(dtype)
+    q = (torch.randn((B, 1, 64), generator=g) / 8).to(dtype)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 2048, n_ctx=nc, cap=2050)
+    torch.cuda.synchronize()
+    assert counts[:, 0].cpu().tolist() == [0, 1, 2047, 2048, 2048, 2048]
+    assert bool((idx[0] == -1).all()) and idx[1, 0, 0].item() == 0
+    _check(idx, counts, q, K, n_ctx, -1, 2048, 2050)
+    idx1, counts1 = clsa.route(q.to(DEV), K.to(DEV), 1, n_ctx=nc, cap=3)
+    torch.cuda.synchronize()
+    assert counts1[:, 0].cpu().tolist() == [0, 1, 1, 1, 1, 1]
+    _check(idx1, counts1, q, K, n_ctx, -1, 1, 3)
