@@ -1,7 +1,7 @@
 """The library's host-side code under AddressSanitizer and
 UndefinedBehaviorSanitizer, on the CPU.
 
-The four sources are compiled as in the normal build, with the sanitizers on
+The library sources are compiled as in the normal build, with the sanitizers on
 the host pass only (each -fsanitize= right after -Xarch_host, so no device
 code is instrumented), and linked into tests/abi_host_driver.cpp.  The
 driver calls every entry point over shapes up to and past each limit:
