@@ -179,7 +179,9 @@ CLSA_DEV void group_reduce(float (&v)[NV], int lane, int& base) {
 constexpr int kWaves = 4;
 // scores of one workgroup live in LDS: G heads x TS tokens of fp32
 constexpr int kScoreFloats = 8192;
-__host__ __device__ constexpr int ts_max(int G) { return kScoreFloats / G; }
+// (at most 2048 tokens, so that groups of one or two query heads still fit
+// four workgroups' LDS per CU)
+__host__ __device__ constexpr int ts_max(int G) { return kScoreFloats / G < 2048 ? kScoreFloats / G : 2048; }
 
 // Workgroup = (split s, KV head g) x row r x layer l; blockIdx.x = s*Hkv + g.
 // Every lane owns 8 consecutive dims (16 bytes) of one token slot, so one

@@ -846,7 +846,8 @@ int block_route(const void* q_idx, const void* K_idx, int B, int M, int d, int64
 // Few query rows per sequence (decode): the threshold and the select of
 // block routing around a streaming score pass (clsa_route.hip) that writes
 // the candidates of each key chunk into that chunk's segment.
-bool seg_route_applies(int M, int d, int64_t n_cap, int k, clsa_dtype dt) {
+bool seg_route_applies(int /* M: every row count below block routing's qualifies */, int d,
+                       int64_t n_cap, int k, clsa_dtype dt) {
   if (dt != CLSA_BF16 || k > kMaxK) return false;
   if (d != 32 && d != 64 && d != 128) return false;
   return n_cap <= kMaxKeys;
