@@ -719,33 +719,39 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
     return;
   }
 
-  // thread t holds candidates t, t + kNT, ...: a wave's loads cover
-  // consecutive entries (coalesced).  Each element's segment (the last one
-  // starting at or before it) is found by binary lifting over the offsets,
-  // all of the thread's searches in step so that each step waits on LDS once.
-  const int cnt = (int)((n_c + kNT - 1 - (uint32_t)tid) / kNT);  // elements of this thread
+  // thread t holds the contiguous run of candidates [t * per, t * per + cnt)
+  // of the row's concatenated segments.  One binary-lifting search over the
+  // offsets finds the segment of the run's first element (the last segment
+  // starting at or before it); the rest of the run walks forward from there,
+  // passing a segment end at most a few times.  (A search per element, all
+  // kPerT in step, cost the kernel a third of its vector instructions.)
+  const uint32_t per = (n_c + kNT - 1) / kNT;  // <= kPerT: n_c <= kSelCap
+  const uint32_t e0 = (uint32_t)tid * per;
+  const int cnt = e0 < n_c ? (int)(n_c - e0 < per ? n_c - e0 : per) : 0;
   uint32_t key[kPerT], pos[kPerT];
   {
-    int lo[kPerT];
-#pragma unroll
-    for (int u = 0; u < kPerT; ++u) lo[u] = 0;
-    int step = 1;
-    while (2 * step < nseg) step *= 2;
-    for (; step > 0; step >>= 1) {
-      uint32_t sv[kPerT];
-#pragma unroll
-      for (int u = 0; u < kPerT; ++u) {
-        const int t = lo[u] + step;
-        sv[u] = segoff[t < nseg ? t : nseg];  // segoff[nseg] = n_c: never taken
+    int c = 0;
+    if (cnt > 0) {
+      int step = 1;
+      while (2 * step < nseg) step *= 2;
+      for (; step > 0; step >>= 1) {
+        const int t = c + step;
+        c = segoff[t < nseg ? t : nseg] <= e0 ? t : c;  // segoff[nseg] = n_c: never taken
       }
-#pragma unroll
-      for (int u = 0; u < kPerT; ++u)
-        lo[u] = sv[u] <= (uint32_t)(u * kNT + tid) ? lo[u] + step : lo[u];
     }
+    uint32_t start = segoff[c], next = segoff[c + 1];  // c < nseg
     uint32_t off[kPerT];
 #pragma unroll
-    for (int u = 0; u < kPerT; ++u)
-      off[u] = (uint32_t)lo[u] * half + ((uint32_t)(u * kNT + tid) - segoff[lo[u]]);
+    for (int u = 0; u < kPerT; ++u) {
+      const uint32_t e = e0 + (uint32_t)u;
+      if (u < cnt)
+        while (next <= e) {  // ends: segoff[nseg] = n_c > e
+          ++c;
+          start = next;
+          next = segoff[c + 1];
+        }
+      off[u] = (uint32_t)c * half + (e - start);
+    }
     const uint64_t* rowseg =
         a.seg + (size_t)r * (ROWSEG ? (size_t)a.nchunks * a.segcap : (size_t)nseg * half);
     uint64_t e[kPerT];
