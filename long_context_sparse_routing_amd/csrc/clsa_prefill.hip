@@ -169,10 +169,10 @@ CLSA_DEV uint32_t select_key_desc(Get get, uint32_t n, uint32_t rank, uint32_t* 
 // ------------------------------------------------------------------ thresh
 // One workgroup per 16 query rows.  Scores against every a.ss-th key come
 // from v_mfma_f32_16x16x32_bf16; as they come out of the accumulator, each
-// lane keeps, per row, the 8 largest top-16-bit prefixes of their
-// order-preserving keys among the samples it sees (an insertion chain: slot
-// i becomes the median of slot i-1, slot i and the new value).  The 128
-// such lists of a row (8 waves x 16 sample lanes, 1024 prefixes) go to LDS,
+// lane keeps, per row, the 8 largest scores among the samples it sees (an
+// insertion chain: slot i becomes the median of slot i-1, slot i and the
+// new value) and stores their top-16-bit order-preserving key prefixes.
+// The 128 such lists of a row (8 waves x 16 sample lanes, 1024 prefixes) go to LDS,
 // and a wave ranks each of its rows' lists: a 1024-bin histogram over their
 // actual range and a second pass over the boundary bin give the rho-th
 // largest.  The lists are samples, so that prefix is at most the rho-th
@@ -218,11 +218,15 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
     const int m = m0 + 4 * (lane / 16) + j;
     lim[j] = m < a.M ? row_visible(a, b, m) : 0;
   }
-  uint32_t t8[4][kThrTop];  // per row: this lane's largest prefixes, descending; 0 = none
+  // per row: this lane's largest scores, descending; -inf = none.  The
+  // 16-bit key prefix is a monotone map of the score, so the largest
+  // prefixes are the prefixes of the largest scores: the lists hold floats
+  // (one v_med3_f32 per slot and sample) and are mapped once at the end.
+  float t8[4][kThrTop];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int i = 0; i < kThrTop; ++i) t8[j][i] = 0u;
+    for (int i = 0; i < kThrTop; ++i) t8[j][i] = -INFINITY;
   const int ntile = (a.ns_max + 15) / 16;
   for (int t0 = w * kThrTiles; t0 < ntile; t0 += (kNT / kWave) * kThrTiles) {
     bf16x8_t kb[kThrTiles][D / 32];
@@ -250,13 +254,14 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
       const bool in = t0 + u < ntile && smp < a.ns_max;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t x = (in && j < lim[jj]) ? score_key(c[jj]) >> 16 : 0u;
+        // a NaN score counts as no sample (fmaxf returns the other operand)
+        const float x = (in && j < lim[jj]) ? fmaxf(c[jj], -INFINITY) : -INFINITY;
+        // slot i becomes the median of slot i-1, slot i and x (the list is
+        // sorted, so that is max(slot i, min(slot i-1, x)))
 #pragma unroll
-        for (int i = kThrTop - 1; i >= 1; --i) {
-          const uint32_t lo = t8[jj][i - 1] < x ? t8[jj][i - 1] : x;
-          t8[jj][i] = t8[jj][i] > lo ? t8[jj][i] : lo;
-        }
-        t8[jj][0] = t8[jj][0] > x ? t8[jj][0] : x;
+        for (int i = kThrTop - 1; i >= 1; --i)
+          t8[jj][i] = __builtin_amdgcn_fmed3f(t8[jj][i - 1], t8[jj][i], x);
+        t8[jj][0] = fmaxf(t8[jj][0], x);
       }
     }
   }
@@ -266,7 +271,8 @@ __global__ __launch_bounds__(kNT) void block_thresh(BlockArgs a) {
     if (rl < kThrRows) {
       uint16_t* dst = &kept[rl][(w * 16 + lane % 16) * kThrTop];
 #pragma unroll
-      for (int i = 0; i < kThrTop; ++i) dst[i] = (uint16_t)t8[jj][i];
+      for (int i = 0; i < kThrTop; ++i)
+        dst[i] = t8[jj][i] == -INFINITY ? (uint16_t)0 : (uint16_t)(score_key(t8[jj][i]) >> 16);
     }
   }
   __syncthreads();
