@@ -154,3 +154,21 @@ def test_block_route_workload_rows_sampled_across_the_chunk():
     assert nd <= 2 * len(rows)
     del K_idx
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("M", [1, 64])
+def test_route_empty_middle_segments(M):
+    # keys in the middle of the context score about 0, far below every row's
+    # threshold, so the chunks there hold no candidates and the select walks
+    # its candidate runs across several empty segments (M = 1: decode rows,
+    # 256-key chunks; M = 64: block routing, 2048-key chunks)
+    g = _gen(500 + M)
+    B, n, d, k = 2, 20000, 64, 512
+    K = torch.randn((B, n, d), generator=g)
+    K[:, 6000:14500] *= 1e-3
+    K = K.to(torch.bfloat16)
+    q = (torch.randn((B, M, d), generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), k)
+    torch.cuda.synchronize()
+    _check(idx, counts, q, K, [n, n], -1, k, k)
+    assert not bool(((idx >= 6000) & (idx < 14500)).any())
