@@ -77,7 +77,7 @@ def per_layer_launches(wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos
     the rest of each layer in between.  The steps are the decode run's last
     `steps` ones again (their appends rewrite the same rows), launched
     eagerly with every call marshalled beforehand, as in the headline loop:
-    capturing each step as HIP graphs measured slower on this GPU.  One pass
+    capturing each step as HIP graphs measured slower on the MI355X.  One pass
     is timed by the wall clock; a second one brackets each step's L
     attention calls with HIP events.  A repeat of the last step must
     reproduce its outputs bit for bit."""
