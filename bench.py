@@ -78,9 +78,10 @@ def per_layer_launches(wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos
     `steps` ones again (their appends rewrite the same rows), launched
     eagerly with every call marshalled beforehand, as in the headline loop:
     capturing each step as HIP graphs measured slower on the MI355X.  One pass
-    is timed by the wall clock; a second one brackets each step's L
-    attention calls with HIP events.  A repeat of the last step must
-    reproduce its outputs bit for bit."""
+    is timed by the wall clock; a second one brackets the L attention calls
+    of every 4th step with HIP events (each recorded pair adds a few
+    microseconds to its step).  A repeat of the last step must reproduce
+    its outputs bit for bit."""
     import torch
     new_kidx, new_k, new_v = new_rows
     total = len(q_all)
@@ -107,16 +108,19 @@ def per_layer_launches(wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in T]
 
+    ev_every = 4
+
     def run(events):
         with torch.cuda.stream(s):
             for i, (pre, layers) in enumerate(calls):
+                mark = events and i % ev_every == 0
                 for c in pre:
                     c()
-                if events:
+                if mark:
                     ev[i][0].record(s)
                 for c in layers:
                     c()
-                if events:
+                if mark:
                     ev[i][1].record(s)
 
     torch.cuda.synchronize()
@@ -132,14 +136,15 @@ def per_layer_launches(wl, clsa, K_idx, Kc, Vc, q_idx_all, q_all, n_ctx_all, pos
         raise RuntimeError("a repeat of the per-layer steps changed the last step's outputs")
     run(True)
     s.synchronize()
-    attn_ms = sum(a.elapsed_time(b) for a, b in ev) / len(T)
+    marked = [ev[i] for i in range(len(T)) if i % ev_every == 0]
+    attn_ms = sum(a.elapsed_time(b) for a, b in marked) / len(marked)
     ms = wall * 1e3 / len(T)
     return {"steps": len(T), "ms_per_step": ms, "tokens_per_s": wl.B * len(T) / wall,
             "attn_ms_per_step": attn_ms, "attn_ms_per_layer": attn_ms / wl.L,
             "repeat_matches": same,
             "note": "append + route + one clsa_sparse_attn call per layer, launched eagerly; "
-                    "attention time from events on a second pass; the headline value launches "
-                    "the 16 layers' attention as one call"}
+                    "attention time from events on every 4th step of a second pass; the "
+                    "headline value launches the 16 layers' attention as one call"}
 
 
 def _blas_threads():
