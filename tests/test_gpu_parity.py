@@ -320,6 +320,43 @@ def test_attn_out_of_range_entries_are_skipped():
         assert np.max(np.abs(f64(out[0, 0, m]) - o_out[0, 0, 0])) <= 2e-2
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [(torch.bfloat16, 32, 8, 128),
+                                            (torch.bfloat16, 16, 8, 64),
+                                            (torch.float32, 4, 2, 64)])
+def test_attn_duplicate_and_unordered_entries(dtype, Hq, Hkv, D):
+    # a list is a sequence, not a set: a position listed twice takes two
+    # softmax terms, and the order of the entries does not matter.  Row
+    # lengths cover one ragged tile, several tiles and a split row.
+    g = _cpu_gen(29)
+    L, B, M, n_cap, cap = 2, 2, 3, 700, 2048
+    q = torch.randn((L, B, M, Hq, D), generator=g).to(dtype)
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    idx = torch.full((B, M, cap), -1, dtype=torch.int32)
+    counts = torch.zeros((B, M), dtype=torch.int32)
+    lens = [37, 300, 2048, 129, 1500, 1]
+    for r, c in enumerate(lens):
+        b, m = divmod(r, M)
+        # positions drawn with replacement from a small pool, so many repeat
+        pool = torch.randperm(n_cap, generator=g)[: max(1, c // 3)]
+        sel = pool[torch.randint(0, pool.numel(), (c,), generator=g)]
+        idx[b, m, :c] = sel.to(torch.int32)
+        counts[b, m] = c
+    assert any(torch.unique(idx[b, m, : counts[b, m]]).numel() < int(counts[b, m])
+               for b in range(B) for m in range(M) if counts[b, m] > 1)
+    _check_attn(q, K, V, idx, counts)
+    # the same multiset in ascending order gives the same output within
+    # rounding of the summation order
+    srt = idx.clone()
+    for b in range(B):
+        for m in range(M):
+            c = int(counts[b, m])
+            srt[b, m, :c] = idx[b, m, :c].sort().values
+    a, _ = clsa.sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), counts.to(DEV))
+    s, _ = clsa.sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), srt.to(DEV), counts.to(DEV))
+    assert np.max(np.abs(f64(a) - f64(s))) <= ATOL[dtype]
+
+
 def test_attn_split_rows_with_empty_splits():
     # one query row per layer is split 8 ways (256 entries each); in row 0
     # the second half of the list is -1, so four splits hold nothing and the
