@@ -357,6 +357,91 @@ def test_attn_duplicate_and_unordered_entries(dtype, Hq, Hkv, D):
     assert np.max(np.abs(f64(a) - f64(s))) <= ATOL[dtype]
 
 
+def _vector_lists(g, R, n_cap, cap, counts):
+    """R ascending lists of `cap` distinct positions (all slots filled)."""
+    sel = torch.rand((R, n_cap), generator=g).argsort(dim=1)[:, :cap].sort(dim=1).values
+    return sel.to(torch.int32), torch.as_tensor(counts, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_attn_most_layers(dtype):
+    # L = 64, the most layers one call takes; two rows, one split per row
+    # and one list that splits
+    g = _cpu_gen(30)
+    L, B, M, Hq, Hkv, D, n_cap, cap = 64, 1, 2, 8, 2, 64, 3000, 1500
+    q = torch.randn((L, B, M, Hq, D), generator=g).to(dtype)
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    idx, counts = _vector_lists(g, B * M, n_cap, cap, [1500, 200])
+    _check_attn(q, K, V, idx.view(B, M, cap), counts.view(B, M))
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_attn_most_rows(dtype):
+    # B*M = 65535 rows, the grid's limit; checked on the first, the last and
+    # a spread of rows between
+    g = _cpu_gen(31)
+    L, B, M, Hq, Hkv, D, n_cap, cap = 2, 5, 13107, 4, 1, 64, 96, 24
+    R = B * M
+    q = torch.randn((L, B, M, Hq, D), generator=g).to(dtype)
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    cnt = torch.randint(0, cap + 1, (R,), generator=g)
+    cnt[-1] = cap
+    idx, counts = _vector_lists(g, R, n_cap, cap, cnt)
+    idx, counts = idx.view(B, M, cap), counts.view(B, M)
+    out, lse = clsa.sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), counts.to(DEV),
+                                want_lse=True)
+    picks = sorted({0, 1, R - 2, R - 1, *range(0, R, 331)})
+    rows = [divmod(r, M) for r in picks]
+    o_out, o_lse = O.sparse_attn([f64(q[l]) for l in range(L)], [f64(K[l]) for l in range(L)],
+                                 [f64(V[l]) for l in range(L)], idx.numpy(), counts.numpy(), cap,
+                                 rows=rows)
+    go, gl = f64(out), f64(lse)
+    for b, m in rows:
+        assert np.max(np.abs(go[:, b, m] - o_out[:, b, m])) <= ATOL[dtype], (b, m)
+        fin = np.isfinite(o_lse[:, b, m])
+        assert np.array_equal(np.isfinite(gl[:, b, m]), fin)
+        assert np.max(np.abs(gl[:, b, m][fin] - o_lse[:, b, m][fin]), initial=0.0) <= 1e-3
+    assert len(rows) >= 200
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [(torch.bfloat16, 64, 64, 128),
+                                            (torch.float32, 64, 64, 128),
+                                            (torch.bfloat16, 32, 4, 256),
+                                            (torch.float32, 32, 4, 256)])
+def test_attn_widest_heads(dtype, Hq, Hkv, D):
+    # Hq * D = 8192, the widest query a call takes: 64 heads of 128 (every
+    # query head its own KV head) and 32 heads of 256 in groups of 8
+    g = _cpu_gen(32)
+    L, B, M, n_cap, cap = 2, 2, 2, 1200, 700
+    q = torch.randn((L, B, M, Hq, D), generator=g).to(dtype)
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    idx, counts = _vector_lists(g, B * M, n_cap, cap, [700, 1, 333, 0])
+    _check_attn(q, K, V, idx.view(B, M, cap), counts.view(B, M))
+
+
+def test_attn_counts_past_cap_use_the_first_cap_entries():
+    # a threshold list longer than cap reports its true size; attention
+    # takes the first cap entries, as for counts == cap
+    g = _cpu_gen(33)
+    L, B, M, Hq, Hkv, D, n_cap, cap = 2, 1, 3, 32, 8, 128, 5000, 640
+    q = torch.randn((L, B, M, Hq, D), generator=g).to(torch.bfloat16)
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(torch.bfloat16)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(torch.bfloat16)
+    idx, _ = _vector_lists(g, M, n_cap, cap, [0, 0, 0])
+    idx = idx.view(B, M, cap)
+    over = torch.tensor([[641, 100000, 2 ** 31 - 1]], dtype=torch.int32)
+    at = torch.full((B, M), cap, dtype=torch.int32)
+    a, la = clsa.sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), over.to(DEV),
+                             want_lse=True)
+    b_, lb = clsa.sparse_attn(q.to(DEV), K.to(DEV), V.to(DEV), idx.to(DEV), at.to(DEV),
+                              want_lse=True)
+    assert torch.equal(a, b_) and torch.equal(la, lb)
+    _check_attn(q, K, V, idx, at)
+
+
 def test_attn_split_rows_with_empty_splits():
     # one query row per layer is split 8 ways (256 entries each); in row 0
     # the second half of the list is -1, so four splits hold nothing and the
