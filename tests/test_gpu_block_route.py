@@ -172,3 +172,18 @@ def test_route_empty_middle_segments(M):
     torch.cuda.synchronize()
     _check(idx, counts, q, K, [n, n], -1, k, k)
     assert not bool(((idx >= 6000) & (idx < 14500)).any())
+
+
+def test_block_route_most_rows():
+    # B*M = 65535 rows, the call's limit, in one causal block from position
+    # 0: early rows keep every visible key, rows past 8191 the top 64 of 8192
+    g = _gen(600)
+    M, n, d, k = 65535, 8192, 64, 64
+    K = torch.randn((1, n, d), generator=g).to(torch.bfloat16)
+    q = (torch.randn((1, M, d), generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), k, q_pos0=0)
+    torch.cuda.synchronize()
+    assert counts[0, :64].cpu().tolist() == list(range(1, 65))
+    ms = sorted({0, 1, 62, 63, 64, 255, 256, 8190, 8191, 8192, M - 2, M - 1,
+                 *range(5, M, 997)})
+    _check(idx, counts, q, K, [n], 0, k, k, [(0, m) for m in ms])

@@ -137,3 +137,23 @@ def test_empty_and_tiny_contexts(dtype):
     torch.cuda.synchronize()
     assert counts1[:, 0].cpu().tolist() == [0, 1, 1, 1, 1, 1]
     _check(idx1, counts1, q, K, n_ctx, -1, 1, 3)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_most_sequences_one_call(dtype):
+    # B = 65535 sequences of one query each, the call's row limit, with
+    # contexts of 0 .. 300 keys (below, at and above k); checked on the
+    # first, the last and a spread of sequences between
+    gd = torch.Generator(device=DEV)
+    gd.manual_seed(970)
+    B, n, d, k = 65535, 300, 32, 16
+    K = torch.randn((B, n, d), generator=gd, device=DEV).to(dtype)
+    q = (torch.randn((B, 1, d), generator=gd, device=DEV) / 6).to(dtype)
+    n_ctx = [b % (n + 1) for b in range(B)]
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q, K, k, n_ctx=nc)
+    torch.cuda.synchronize()
+    bs = sorted({0, 1, 15, 16, 17, 300, 301, B - 2, B - 1, *range(7, B, 613)})
+    sel = torch.tensor(bs, device=DEV)
+    _check(idx[sel], counts[sel], q[sel].cpu(), K[sel].cpu(), [n_ctx[b] for b in bs], -1, k, k)
+    assert len(bs) >= 100
