@@ -187,7 +187,9 @@ int clsa_route_threshold(const void* q_idx, const void* K_idx, int B, int M, int
  *   K[l], V[l] [B][n_cap][Hkv][D]  key/value cache of layer l, token-major.
  *   idx    [B][M][cap] int32, counts [B][M] int32: as written by clsa_route
  *          or clsa_route_threshold.  Row (b, m) attends over its first
- *          min(counts, cap) entries; entries outside [0, n_cap) are skipped.
+ *          min(counts, cap) entries (none if counts < 0); entries outside
+ *          [0, n_cap) are padding and skipped; a position listed twice
+ *          counts twice in the softmax.
  *   scale  logit scale; 0 means 1/sqrt(D).
  *   out[l] [B][M][Hq][D] out, dtype of V.
  *   lse    [L][B][M][Hq] float out (natural log-sum-exp of the scaled

@@ -39,6 +39,10 @@ pages supports):
 * R10    threshold mode keeps s >= tau, tau given as float32 and widened;
 * R11    an empty selection gives output 0 and lse = -inf;
 * R12    -0.0 and +0.0 scores are equal (float64 comparison does this).
+* R24    a list passed to attention is read up to min(count, cap) entries
+         (a negative count reads none); entries outside [0, n_cap) are
+         padding, like the -1 that pads a returned list, and take no
+         part in the softmax.
 
 Parity pins live in tests/test_oracle_pins.py.
 """
@@ -202,7 +206,7 @@ def sparse_attn(q, K, V, idx, counts, cap: int, scale: float = 0.0, rows=None, l
     """
     L = len(q)
     B, M, Hq, D = q[0].shape
-    Hkv = K[0].shape[2]
+    n_cap, Hkv = K[0].shape[1], K[0].shape[2]
     sc = float(scale) if scale else 1.0 / math.sqrt(D)
     out = np.zeros((L, B, M, Hq, D), dtype=np.float64)
     lse = np.full((L, B, M, Hq), -math.inf, dtype=np.float64)
@@ -210,8 +214,9 @@ def sparse_attn(q, K, V, idx, counts, cap: int, scale: float = 0.0, rows=None, l
     lays = layers if layers is not None else range(L)
     for l in lays:
         for b, m in todo:
-            n = int(min(counts[b, m], cap))
+            n = max(0, int(min(counts[b, m], cap)))
             sel = np.asarray(idx[b, m, :n], dtype=np.int64)
+            sel = sel[(sel >= 0) & (sel < n_cap)]  # padding entries (R24)
             Kr = np.asarray(K[l][b][sel], dtype=np.float64)  # [n, Hkv, D]
             Vr = np.asarray(V[l][b][sel], dtype=np.float64)
             for h in range(Hq):

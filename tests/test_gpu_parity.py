@@ -357,6 +357,27 @@ def test_attn_duplicate_and_unordered_entries(dtype, Hq, Hkv, D):
     assert np.max(np.abs(f64(a) - f64(s))) <= ATOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,Hq,Hkv,D", [(torch.bfloat16, 32, 8, 128),
+                                            (torch.float32, 8, 2, 64)])
+def test_attn_padding_entries_and_odd_counts(dtype, Hq, Hkv, D):
+    # lists built outside the routing calls (reading R24 of the oracle):
+    # padding entries (-1, n_cap, the int32 extremes) inside the counted
+    # prefix, repeated positions, negative counts, counts past cap; the
+    # oracle reads the same lists by the same rules, and rows split
+    g = _cpu_gen(34)
+    L, B, M, n_cap, cap = 2, 2, 4, 900, 600
+    q = torch.randn((L, B, M, Hq, D), generator=g).to(dtype)
+    K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(dtype)
+    idx = torch.randint(0, n_cap, (B, M, cap), generator=g, dtype=torch.int32)
+    pad = torch.rand((B, M, cap), generator=g) < 0.1
+    vals = torch.tensor([-1, n_cap, 2 ** 31 - 1, -2 ** 31], dtype=torch.int32)
+    idx[pad] = vals[torch.randint(0, 4, (int(pad.sum()),), generator=g)]
+    idx[1, 1, 0] = -1  # a count of 1 over padding only: an empty row
+    counts = torch.tensor([[600, -1, 257, 10 ** 6], [-2 ** 31, 1, 599, 0]], dtype=torch.int32)
+    _check_attn(q, K, V, idx, counts)
+
+
 def _vector_lists(g, R, n_cap, cap, counts):
     """R ascending lists of `cap` distinct positions (all slots filled)."""
     sel = torch.rand((R, n_cap), generator=g).argsort(dim=1)[:, :cap].sort(dim=1).values

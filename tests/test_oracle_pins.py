@@ -54,6 +54,7 @@ def _ns(**over):
 ORACLE = _ns()
 # originals, for mutants that wrap them (the mutation tests patch the module)
 _SCORES, _TOPK, _ATTEND = O.route_scores, O.topk_select, O.attend_head
+_SPARSE = O.sparse_attn
 
 
 def _bf16_values(shape, rng, scale=1.0):
@@ -317,6 +318,42 @@ def pin_prefill_visibility(o):
     assert counts[0, 4] == 5 and idx[0, 4, :5].tolist() == [0, 1, 2, 3, 4]
 
 
+def pin_attention_padding_and_counts(o):
+    # R24: a list is read up to min(count, cap) entries, a negative count
+    # reads none, entries outside [0, n_cap) are padding, and a position
+    # listed c times weighs c times in the softmax.  Reference: dense SDPA
+    # with log(multiplicity) as the additive mask of each listed position.
+    rng = np.random.default_rng(21)
+    q, K, V = _rand_attn_case(rng, L=1, B=1, M=6)
+    N, cap, sc = 37, 12, 0.3
+    idx = rng.integers(0, N, size=(1, 6, cap))
+    idx[0, 0, [1, 4, 7]] = -1          # padding inside the counted prefix
+    idx[0, 1, [0, 11]] = N             # one past the end, and at the last slot
+    idx[0, 2, :6] = [5, 5, 5, 9, 9, 2]  # repeats
+    counts = np.array([[cap, cap, 6, -3, cap + 40, 4]])
+    idx[0, 5, :4] = -1                 # a counted prefix of padding only
+    out, lse = o.sparse_attn(q, K, V, idx, counts, cap, scale=sc)
+    for m in range(6):
+        n = max(0, min(int(counts[0, m]), cap))
+        ent = [int(j) for j in idx[0, m, :n] if 0 <= j < N]
+        if not ent:
+            assert np.all(out[0, 0, m] == 0) and np.all(lse[0, 0, m] == -math.inf), m
+            continue
+        mult = np.bincount(ent, minlength=N)
+        mask = torch.full((1, 8, 1, N), -math.inf, dtype=torch.float64)
+        mask[0, :, 0, mult > 0] = torch.from_numpy(np.log(mult[mult > 0]))
+        qq = torch.from_numpy(q[0][0, m:m + 1]).permute(1, 0, 2)[None]
+        kk = torch.from_numpy(K[0][0]).permute(1, 0, 2).repeat_interleave(4, 0)[None]
+        vv = torch.from_numpy(V[0][0]).permute(1, 0, 2).repeat_interleave(4, 0)[None]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, attn_mask=mask,
+                                                               scale=sc)[0, :, 0].numpy()
+        assert np.max(np.abs(out[0, 0, m] - ref)) < 1e-12, m
+        for h in range(8):
+            z = (K[0][0][:, h // 4, :] @ q[0][0, m, h]) * sc
+            want = math.log(float(np.sum(mult * np.exp(z))))
+            assert abs(lse[0, 0, m, h] - want) < 1e-12, (m, h)
+
+
 ALL_PINS = [
     pin_golden,
     pin_scores_exact,
@@ -330,6 +367,7 @@ ALL_PINS = [
     pin_softmax_weights,
     pin_attention_closed_forms,
     pin_attention_hull_and_order,
+    pin_attention_padding_and_counts,
     pin_prefill_visibility,
 ]
 
@@ -461,6 +499,19 @@ def _mut_attend_lse_no_max(q, K, V, scale, return_weights=False):
     return (out, wrong, p) if return_weights else (out, wrong)
 
 
+def _mut_attn_padding_as_rows(q, K, V, idx, counts, cap, scale=0.0, rows=None, layers=None):
+    # padding entries wrapped around to real rows
+    n_cap = K[0].shape[1]
+    return _SPARSE(q, K, V, np.mod(idx, n_cap), counts, cap, scale, rows, layers)
+
+
+def _mut_attn_negative_count_slices(q, K, V, idx, counts, cap, scale=0.0, rows=None,
+                                    layers=None):
+    # a negative count read as a slice end counted from the back
+    c = np.where(np.asarray(counts) < 0, cap + np.asarray(counts), counts)
+    return _SPARSE(q, K, V, idx, c, cap, scale, rows, layers)
+
+
 MUTANTS = {
     "scores_drop_last_term": dict(route_scores=_mut_scores_drop_last),
     "scores_off_by_one_visible": dict(route_scores=_mut_scores_off_by_one),
@@ -472,6 +523,8 @@ MUTANTS = {
     "attend_missing_scale": dict(attend_head=_mut_attend_no_scale),
     "attend_no_max_subtraction": dict(attend_head=_mut_attend_no_max),
     "attend_lse_missing_max": dict(attend_head=_mut_attend_lse_no_max),
+    "attn_padding_as_rows": dict(sparse_attn=_mut_attn_padding_as_rows),
+    "attn_negative_count_slices": dict(sparse_attn=_mut_attn_negative_count_slices),
 }
 
 
