@@ -38,11 +38,13 @@ pages supports):
 * R8     in a prefill chunk, the query at absolute position p sees keys 0..p;
 * R10    threshold mode keeps s >= tau, tau given as float32 and widened;
 * R11    an empty selection gives output 0 and lse = -inf;
-* R12    -0.0 and +0.0 scores are equal (float64 comparison does this).
+* R12    -0.0 and +0.0 scores are equal (float64 comparison does this);
 * R24    a list passed to attention is read up to min(count, cap) entries
          (a negative count reads none); entries outside [0, n_cap) are
          padding, like the -1 that pads a returned list, and take no
-         part in the softmax.
+         part in the softmax; a position listed twice counts twice;
+* R25    a context length n_ctx[b] outside [0, n_cap] is taken as the
+         nearest end of that range.
 
 Parity pins live in tests/test_oracle_pins.py.
 """
@@ -143,12 +145,16 @@ def attend_head(q_h, K_sel, V_sel, scale: float, return_weights: bool = False):
 # ---------------------------------------------------------------------------
 # Batched wrappers with the library's shapes
 # ---------------------------------------------------------------------------
-def visible_count(n_ctx_b: int, q_pos0: int, m: int) -> int:
+def visible_count(n_ctx_b: int, q_pos0: int, m: int, n_cap: int | None = None) -> int:
     """Keys visible to query row m: the whole context in decode (q_pos0 < 0),
-    keys 0..q_pos0+m in a prefill chunk (reading R8)."""
+    keys 0..q_pos0+m in a prefill chunk (reading R8); a context length
+    outside [0, n_cap] counts as the nearest end of that range (R25)."""
+    n = max(0, int(n_ctx_b))
+    if n_cap is not None:
+        n = min(n, int(n_cap))
     if q_pos0 < 0:
-        return int(n_ctx_b)
-    return int(min(n_ctx_b, q_pos0 + m + 1))
+        return n
+    return int(min(n, q_pos0 + m + 1))
 
 
 def route(q_idx, K_idx, n_ctx, q_pos0: int, k: int, cap: int, rows=None):
@@ -163,7 +169,7 @@ def route(q_idx, K_idx, n_ctx, q_pos0: int, k: int, cap: int, rows=None):
     counts = np.zeros((B, M), dtype=np.int64)
     todo = rows if rows is not None else [(b, m) for b in range(B) for m in range(M)]
     for b, m in todo:
-        nv = visible_count(n_ctx[b], q_pos0, m)
+        nv = visible_count(n_ctx[b], q_pos0, m, K_idx.shape[1])
         s = route_scores(q_idx[b, m], K_idx[b], nv)
         sel = topk_select(s, k)
         idx[b, m, : sel.shape[0]] = sel
@@ -182,7 +188,7 @@ def route_threshold(q_idx, K_idx, n_ctx, q_pos0: int, tau, cap: int, rows=None):
     counts = np.zeros((B, M), dtype=np.int64)
     todo = rows if rows is not None else [(b, m) for b in range(B) for m in range(M)]
     for b, m in todo:
-        nv = visible_count(n_ctx[b], q_pos0, m)
+        nv = visible_count(n_ctx[b], q_pos0, m, K_idx.shape[1])
         s = route_scores(q_idx[b, m], K_idx[b], nv)
         sel = threshold_select(s, tau[b, m])
         w = min(cap, sel.shape[0])

@@ -187,3 +187,19 @@ def test_block_route_most_rows():
     ms = sorted({0, 1, 62, 63, 64, 255, 256, 8190, 8191, 8192, M - 2, M - 1,
                  *range(5, M, 997)})
     _check(idx, counts, q, K, [n], 0, k, k, [(0, m) for m in ms])
+
+
+def test_block_route_context_lengths_outside_the_cache():
+    # a block of causal rows whose sequences report context lengths below 0
+    # (no key) or above n_cap (every key up to the row's position), as the
+    # oracle's reading R25 takes them
+    g = _gen(700)
+    B, M, n, d, k = 3, 64, 5000, 64, 300
+    n_ctx = [-7, n + 1000, 2 ** 31 - 1]
+    K = torch.randn((B, n, d), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, M, d), generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), k, n_ctx=nc, q_pos0=4950, cap=k)
+    torch.cuda.synchronize()
+    assert bool((counts[0] == 0).all()) and bool((idx[0] == -1).all())
+    _check(idx, counts, q, K, n_ctx, 4950, k, k)

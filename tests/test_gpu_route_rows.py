@@ -157,3 +157,20 @@ def test_most_sequences_one_call(dtype):
     sel = torch.tensor(bs, device=DEV)
     _check(idx[sel], counts[sel], q[sel].cpu(), K[sel].cpu(), [n_ctx[b] for b in bs], -1, k, k)
     assert len(bs) >= 100
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_context_lengths_outside_the_cache(dtype):
+    # context lengths below 0 see no key and lengths above n_cap every key
+    # (the oracle's reading R25), in one call with ordinary ones
+    g = _gen(980)
+    n = 9000
+    n_ctx = [-1, -(2 ** 31), n + 1, 2 ** 31 - 1, 0, n]
+    B = len(n_ctx)
+    K = torch.randn((B, n, 64), generator=g).to(dtype)
+    q = (torch.randn((B, 1, 64), generator=g) / 8).to(dtype)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    idx, counts = clsa.route(q.to(DEV), K.to(DEV), 2048, n_ctx=nc, cap=2050)
+    torch.cuda.synchronize()
+    assert counts[:, 0].cpu().tolist() == [0, 0, 2048, 2048, 0, 2048]
+    _check(idx, counts, q, K, n_ctx, -1, 2048, 2050)

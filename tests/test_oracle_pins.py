@@ -46,6 +46,7 @@ def _ns(**over):
         attend_head=O.attend_head,
         sparse_attn=O.sparse_attn,
         route=O.route,
+        visible_count=O.visible_count,
     )
     base.update(over)
     return types.SimpleNamespace(**base)
@@ -354,6 +355,29 @@ def pin_attention_padding_and_counts(o):
             assert abs(lse[0, 0, m, h] - want) < 1e-12, (m, h)
 
 
+def pin_context_clamp(o):
+    # R25: a context length below 0 sees no key, one above n_cap every key;
+    # reference: the top-k by a stable argsort of the scores over the keys
+    # the clamped length leaves visible
+    rng = np.random.default_rng(22)
+    n_cap, d, k = 40, 8, 6
+    K = rng.standard_normal((4, n_cap, d))
+    qi = rng.standard_normal((4, 3, d))
+    n_ctx = [-3, n_cap + 50, 5, -(2 ** 31)]
+    for q_pos0 in (-1, 30):
+        idx, counts = o.route(qi, K, n_ctx, q_pos0, k, k + 2)
+        for b, n in enumerate(n_ctx):
+            for m in range(3):
+                nv = min(max(n, 0), n_cap)
+                if q_pos0 >= 0:
+                    nv = min(nv, q_pos0 + m + 1)
+                s_ = K[b, :nv] @ qi[b, m]
+                want = np.sort(np.argsort(-s_, kind="stable")[:k])
+                assert counts[b, m] == len(want), (q_pos0, b, m)
+                assert idx[b, m, : len(want)].tolist() == want.tolist()
+                assert np.all(idx[b, m, len(want):] == -1)
+
+
 ALL_PINS = [
     pin_golden,
     pin_scores_exact,
@@ -369,6 +393,7 @@ ALL_PINS = [
     pin_attention_hull_and_order,
     pin_attention_padding_and_counts,
     pin_prefill_visibility,
+    pin_context_clamp,
 ]
 
 
@@ -512,6 +537,11 @@ def _mut_attn_negative_count_slices(q, K, V, idx, counts, cap, scale=0.0, rows=N
     return _SPARSE(q, K, V, idx, c, cap, scale, rows, layers)
 
 
+def _mut_visible_unclamped(n_ctx_b, q_pos0, m, n_cap=None):
+    # the context length used as given
+    return int(n_ctx_b) if q_pos0 < 0 else int(min(n_ctx_b, q_pos0 + m + 1))
+
+
 MUTANTS = {
     "scores_drop_last_term": dict(route_scores=_mut_scores_drop_last),
     "scores_off_by_one_visible": dict(route_scores=_mut_scores_off_by_one),
@@ -525,6 +555,7 @@ MUTANTS = {
     "attend_lse_missing_max": dict(attend_head=_mut_attend_lse_no_max),
     "attn_padding_as_rows": dict(sparse_attn=_mut_attn_padding_as_rows),
     "attn_negative_count_slices": dict(sparse_attn=_mut_attn_negative_count_slices),
+    "visible_count_unclamped": dict(visible_count=_mut_visible_unclamped),
 }
 
 
