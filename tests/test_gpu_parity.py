@@ -666,14 +666,14 @@ def test_workload_threshold_128k_b16():
 
 def test_kv_append_writes_each_sequence_slot():
     g = _cpu_gen(31)
-    L, B, n_cap, Hkv, D, d = 3, 4, 50, 8, 128, 64
+    L, B, n_cap, Hkv, D, d = 3, 5, 50, 8, 128, 64
     K = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
     V = torch.randn((L, B, n_cap, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
     Ki = torch.randn((B, n_cap, d), generator=g).to(torch.bfloat16).to(DEV)
     nk = torch.randn((L, B, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
     nv = torch.randn((L, B, Hkv, D), generator=g).to(torch.bfloat16).to(DEV)
     ni = torch.randn((B, d), generator=g).to(torch.bfloat16).to(DEV)
-    pos = torch.tensor([0, 17, 49, 50], dtype=torch.int32, device=DEV)  # 50: out of range
+    pos = torch.tensor([0, 17, 49, 50, -1], dtype=torch.int32, device=DEV)  # 50, -1: outside
     K0, V0, Ki0 = K.clone(), V.clone(), Ki.clone()
     clsa.kv_append(pos, ni, Ki, nk, K, nv, V)
     torch.cuda.synchronize()
