@@ -146,10 +146,15 @@ def _check_i32(t: torch.Tensor | None, shape: tuple, name: str):
     _check_shape(t, shape, name)
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
 def _workspace(nbytes: int, device, ws: torch.Tensor | None) -> torch.Tensor:
     if ws is not None:
-        if ws.numel() * ws.element_size() < nbytes:
-            raise ValueError(f"workspace has {ws.numel() * ws.element_size()} bytes, "
+        _check_dev(ws)
+        if _nbytes(ws) < nbytes:
+            raise ValueError(f"workspace has {_nbytes(ws)} bytes, "
                              f"needs {nbytes}")
         return ws
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
@@ -205,7 +210,7 @@ def prepare_route(q_idx: torch.Tensor, K_idx: torch.Tensor, k: int,
     need = lib.clsa_route_workspace_size(B, M, d, n_cap, k, cap, dt)
     ws = _workspace(need, dev, ws)
     args = (_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0, k, dt, _ptr(idx),
-            _ptr(counts), cap, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+            _ptr(counts), cap, _ptr(ws), _nbytes(ws), _stream(stream))
     return Prepared("clsa_route", lib.clsa_route, args, (idx, counts),
                     (q_idx, K_idx, n_ctx, idx, counts, ws))
 
@@ -290,7 +295,7 @@ def prepare_route_threshold(q_idx: torch.Tensor, K_idx: torch.Tensor, tau: torch
     need = lib.clsa_route_threshold_workspace_size(B, M, d, n_cap, cap, dt)
     ws = _workspace(need, dev, ws)
     args = (_ptr(q_idx), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), q_pos0, _ptr(tau), dt,
-            _ptr(idx), _ptr(counts), cap, _ptr(ws), ws.numel() * ws.element_size(),
+            _ptr(idx), _ptr(counts), cap, _ptr(ws), _nbytes(ws),
             _stream(stream))
     return Prepared("clsa_route_threshold", lib.clsa_route_threshold, args, (idx, counts),
                     (q_idx, K_idx, tau, n_ctx, idx, counts, ws))
@@ -355,7 +360,7 @@ def prepare_sparse_attn(q, K, V, idx: torch.Tensor, counts: torch.Tensor, scale:
     va = arr(*[t.data_ptr() for t in Vl])
     oa = arr(*[t.data_ptr() for t in outl])
     args = (L, B, M, Hq, Hkv, D, qa, ka, va, n_cap, _ptr(idx), _ptr(counts), cap, float(scale),
-            dt, oa, _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+            dt, oa, _ptr(lse), _ptr(ws), _nbytes(ws), _stream(stream))
     return Prepared("clsa_sparse_attn", lib.clsa_sparse_attn, args, (out, lse),
                     (ql, Kl, Vl, idx, counts, out, lse, ws))
 
@@ -458,7 +463,7 @@ class LouverIndex:
         ws = _workspace(need, K_idx.device, ws)
         st = lib.clsa_louver_build(_ptr(K_idx), self.B, self.d, K_idx.shape[1], CLSA_BF16, self.S,
                                    self.r, self.n_max, nseg, arr, _ptr(self.buf),
-                                   self.buf.numel(), _ptr(ws), ws.numel(), _stream(stream))
+                                   self.buf.numel(), _ptr(ws), _nbytes(ws), _stream(stream))
         if st != 0:
             raise ClsaError("clsa_louver_build", st)
         self.bounds.append(int(end))
@@ -495,7 +500,7 @@ class LouverIndex:
         ws = _workspace(need, dev, ws)
         args = (_ptr(q_idx), _ptr(K_idx), B, d, n_cap, _ptr(n_ctx), _ptr(tau), _dt(q_idx), self.S,
                 self.r, self.n_max, nseg, arr, _ptr(self.buf), mode, _ptr(idx), _ptr(counts), cap,
-                _ptr(checked), _ptr(ws), ws.numel(), _stream(stream))
+                _ptr(checked), _ptr(ws), _nbytes(ws), _stream(stream))
         return Prepared("clsa_louver_query", lib.clsa_louver_query, args, (idx, counts, checked),
                         (q_idx, K_idx, tau, n_ctx, idx, counts, checked, ws, arr, self.buf))
 
@@ -537,7 +542,7 @@ def prepare_route_aggregated(q_idx, K_idx, k: int, n_ctx: torch.Tensor | None = 
     qa = arr(*[t.data_ptr() for t in ql])
     ka = arr(*[t.data_ptr() for t in Kl])
     args = (H, qa, ka, B, M, d, n_cap, _ptr(n_ctx), q_pos0, k, dt, _ptr(idx), _ptr(counts), cap,
-            _ptr(ws), ws.numel(), _stream(stream))
+            _ptr(ws), _nbytes(ws), _stream(stream))
     return Prepared("clsa_route_aggregated", lib.clsa_route_aggregated, args, (idx, counts),
                     (ql, Kl, n_ctx, idx, counts, ws, qa, ka))
 
@@ -562,7 +567,7 @@ def csa_build(q_prefill: torch.Tensor, K_idx: torch.Tensor, C: int, T: int, roun
     _need(need > 0, f"unsupported centroid table shape B={B} M={M} d={d} C={C} T={T}")
     ws = _workspace(need, dev, ws)
     st = lib.clsa_csa_build(_ptr(q_prefill), _ptr(K_idx), B, M, d, n_cap, _ptr(n_ctx), C, rounds,
-                            T, CLSA_BF16, _ptr(cent), _ptr(table), _ptr(ws), ws.numel(),
+                            T, CLSA_BF16, _ptr(cent), _ptr(table), _ptr(ws), _nbytes(ws),
                             _stream(stream))
     if st != 0:
         raise ClsaError("clsa_csa_build", st)
@@ -595,7 +600,7 @@ def prepare_csa_route(q_idx: torch.Tensor, K_idx: torch.Tensor, centroids: torch
     _check_dev(q_idx, K_idx, centroids, table, n_ctx, idx, counts)
     ws = _workspace(lib.clsa_csa_route_workspace_size(B, d, n_cap, C, T, P), dev, ws)
     args = (_ptr(q_idx), _ptr(K_idx), B, d, n_cap, _ptr(n_ctx), _ptr(centroids), _ptr(table), C, T,
-            n_table, P, k, CLSA_BF16, _ptr(idx), _ptr(counts), cap, _ptr(ws), ws.numel(),
+            n_table, P, k, CLSA_BF16, _ptr(idx), _ptr(counts), cap, _ptr(ws), _nbytes(ws),
             _stream(stream))
     return Prepared("clsa_csa_route", lib.clsa_csa_route, args, (idx, counts),
                     (q_idx, K_idx, centroids, table, n_ctx, idx, counts, ws))

@@ -147,3 +147,34 @@ def test_louver_threshold_workload(clusters):
         assert frac[(1, 1)] < 0.5, frac  # the index prunes on clustered keys
     del Kd
     torch.cuda.empty_cache()
+
+
+def test_louver_workspaces_of_any_element_type():
+    # caller workspaces are sized in bytes whatever their element type: a
+    # float32 buffer of exactly the bytes asked for serves the build and
+    # the query, with the same results as the binding's own buffers
+    g = torch.Generator()
+    g.manual_seed(690)
+    B, n, d = 2, 3000, 64
+    K = torch.randn((B, n, d), generator=g).to(torch.bfloat16)
+    q = (torch.randn((B, 1, d), generator=g) / 8).to(torch.bfloat16)
+    tau = torch.from_numpy(_taus(q, K, [n, n], [20, 300])).to(DEV)
+    Kd, qd = K.to(DEV), q.to(DEV)
+    lib = clsa.load_library()
+
+    def f32_ws(nbytes):
+        assert nbytes % 4 == 0
+        return torch.empty(max(1, nbytes // 4), dtype=torch.float32, device=DEV)
+
+    a, b_ = clsa.LouverIndex(B, d, n, device=DEV), clsa.LouverIndex(B, d, n, device=DEV)
+    a.build(Kd, n)
+    b_.build(Kd, n, ws=f32_ws(lib.clsa_louver_build_workspace_size(B, d, n, 1, 64)))
+    torch.cuda.synchronize()
+    assert torch.equal(a.buf, b_.buf)
+    arr, nseg = b_._bounds()
+    need = lib.clsa_louver_query_workspace_size(B, d, n, 1, 64, n, nseg, arr)
+    ra = a.query(qd, Kd, tau, 512)
+    rb = b_.query(qd, Kd, tau, 512, ws=f32_ws(need))
+    torch.cuda.synchronize()
+    assert torch.equal(ra[0], rb[0]) and torch.equal(ra[1], rb[1])
+    _check(rb[0], rb[1], q, K, [n, n], tau.cpu().numpy(), 512)
