@@ -668,13 +668,13 @@ constexpr int kPerT = kSelCap / kNT;
 
 // Bitmap words each select thread owns (contiguous, a multiple of 4 so they
 // are read 16 bytes at a time); the bitmap covers kNT times that many words
-// and is followed by one prefix word per 4-word group.
+// and is followed by a 16-bit prefix per word.
 __host__ __device__ inline int select_words_per_thread(int64_t n_cap) {
   const int64_t w = ceil_div64(ceil_div64(n_cap, 32), kNT);
   return (int)((w + 3) / 4 * 4);
 }
 inline size_t select_lds_bytes(int64_t n_cap) {
-  return (size_t)select_words_per_thread(n_cap) * kNT * sizeof(uint32_t) * 5 / 4;
+  return select_bitmap_lds_bytes(select_words_per_thread(n_cap));
 }
 
 // The row's candidates sit in segments, one per key chunk, with
@@ -685,7 +685,7 @@ inline size_t select_lds_bytes(int64_t n_cap) {
 // the segment overflowed, and the row is rescanned.
 template <int D, bool ROWSEG>
 __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
-  extern __shared__ u32x4_t bitmap4[];  // select_lds_bytes(n_cap): bitmap, then group prefixes
+  extern __shared__ u32x4_t bitmap4[];  // select_lds_bytes(n_cap): bitmap, then word prefixes
   __shared__ uint32_t segoff[kMaxSegs + 1];
   __shared__ SelScratch S;
   __shared__ uint32_t wcnt[kNT / kWave];

@@ -253,7 +253,7 @@ __global__ __launch_bounds__(256) void csa_score(CsaArgs a) {
 
 // per row: drop duplicate candidates, then the exact top-k in order
 __global__ __launch_bounds__(kSelNT) void csa_select(CsaArgs a) {
-  extern __shared__ u32x4_t bitmap4[];  // positions bitmap + group prefixes
+  extern __shared__ u32x4_t bitmap4[];  // positions bitmap + word prefixes
   uint32_t* bitmap = reinterpret_cast<uint32_t*>(bitmap4);
   __shared__ SelScratch S;
   __shared__ uint32_t tot;
@@ -304,7 +304,7 @@ __global__ __launch_bounds__(kSelNT) void csa_select(CsaArgs a) {
 
 size_t csa_lds_bytes(int64_t n_cap) {
   const int64_t wpt = (ceil_div64(ceil_div64(n_cap, 32), kSelNT) + 3) / 4 * 4;
-  return (size_t)wpt * kSelNT * sizeof(uint32_t) * 5 / 4;
+  return select_bitmap_lds_bytes(wpt);
 }
 
 template <int D>

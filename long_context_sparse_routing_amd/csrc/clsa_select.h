@@ -142,11 +142,19 @@ CLSA_DEV uint32_t kth_regs(const uint32_t (&k)[NPER], int cnt, uint32_t rank, Se
 }
 
 
+// LDS of a select's position bitmap: wpt words per thread, followed by one
+// 16-bit prefix per word (the marks before it; a select marks at most the
+// candidates it holds, far below 65536).
+__host__ __device__ inline size_t select_bitmap_lds_bytes(int64_t wpt) {
+  return (size_t)wpt * kSelNT * (sizeof(uint32_t) + sizeof(uint16_t));
+}
+
 // The k_eff largest of the keys held in registers (thread t: key[u], pos[u]
 // for u < cnt; positions distinct), written to out[0 .. k_eff) in ascending
 // position order; equal keys at the boundary are taken in position order.
-// bitmap4: zeroed LDS bitmap over positions, wpt words per thread followed
-// by one prefix word per 4-word group.  Every thread of the block calls it.
+// bitmap4: zeroed LDS bitmap over positions, wpt words per thread (a
+// multiple of 4), then room for the word prefixes (select_bitmap_lds_bytes).
+// Every thread of the block calls it.
 template <int NPER>
 CLSA_DEV void select_emit(const uint32_t (&key)[NPER], const uint32_t (&pos)[NPER], int cnt,
                           uint32_t k_eff, SelScratch& S, u32x4_t* bitmap4, int wpt, int32_t* out) {
@@ -204,10 +212,10 @@ CLSA_DEV void select_emit(const uint32_t (&key)[NPER], const uint32_t (&pos)[NPE
   __syncthreads();
 
   // emit in position order: the output slot of a selected position is the
-  // number of marked positions below it -- a prefix over 4-word groups of
-  // the bitmap, then popcounts inside the group -- so every thread writes
-  // its own selected candidates independently
-  uint32_t* gpre = bitmap + (size_t)wpt * kSelNT;  // per 4-word group: marks before it
+  // number of marked positions below it -- the prefix of its bitmap word,
+  // then a popcount inside the word -- so every thread writes its own
+  // selected candidates independently
+  uint2* wpre2 = reinterpret_cast<uint2*>(bitmap + (size_t)wpt * kSelNT);  // 4 prefixes each
   uint32_t mine = 0;
   for (int i = w0; i < w0 + wpt; i += 4) {
     const u32x4_t x = bitmap4[i / 4];
@@ -216,22 +224,19 @@ CLSA_DEV void select_emit(const uint32_t (&key)[NPER], const uint32_t (&pos)[NPE
   uint32_t run = block_incl_scan<kSelNT>(mine, S.tmp) - mine;
   for (int i = w0; i < w0 + wpt; i += 4) {
     const u32x4_t x = bitmap4[i / 4];
-    gpre[i / 4] = run;
-    run += __popc(x[0]) + __popc(x[1]) + __popc(x[2]) + __popc(x[3]);
+    const uint32_t r1 = run + __popc(x[0]), r2 = r1 + __popc(x[1]), r3 = r2 + __popc(x[2]);
+    wpre2[i / 4] = make_uint2(run | (r1 << 16), r2 | (r3 << 16));
+    run = r3 + __popc(x[3]);
   }
   __syncthreads();
+  const uint16_t* wpre = reinterpret_cast<const uint16_t*>(wpre2);
 #pragma unroll
   for (int u = 0; u < NPER; ++u) {
     if (u < cnt) {
       const uint32_t p = pos[u];
-      const u32x4_t x = bitmap4[p >> 7];
-      const uint32_t e = (p >> 5) & 3u;
-      const uint32_t word = e == 0 ? x[0] : (e == 1 ? x[1] : (e == 2 ? x[2] : x[3]));
-      if ((word >> (p & 31u)) & 1u) {
-        uint32_t slot = gpre[p >> 7] + __popc(word & ((1u << (p & 31u)) - 1u));
-        slot += (e > 0 ? __popc(x[0]) : 0u) + (e > 1 ? __popc(x[1]) : 0u) + (e > 2 ? __popc(x[2]) : 0u);
-        out[slot] = (int32_t)p;
-      }
+      const uint32_t word = bitmap[p >> 5];
+      if ((word >> (p & 31u)) & 1u)
+        out[wpre[p >> 5] + __popc(word & ((1u << (p & 31u)) - 1u))] = (int32_t)p;
     }
   }
 }
