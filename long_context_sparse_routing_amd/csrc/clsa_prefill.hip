@@ -745,7 +745,9 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
         c = segoff[t < nseg ? t : nseg] <= e0 ? t : c;  // segoff[nseg] = n_c: never taken
       }
     }
+    // element e of segment c sits at c * half + (e - segoff[c]) = e + delta
     uint32_t start = segoff[c], next = segoff[c + 1];  // c < nseg
+    uint32_t delta = (uint32_t)c * half - start;
     uint32_t off[kPerT];
 #pragma unroll
     for (int u = 0; u < kPerT; ++u) {
@@ -753,10 +755,11 @@ __global__ __launch_bounds__(kNT) void block_select(BlockArgs a) {
       if (u < cnt)
         while (next <= e) {  // ends: segoff[nseg] = n_c > e
           ++c;
+          delta += half - (next - start);
           start = next;
           next = segoff[c + 1];
         }
-      off[u] = (uint32_t)c * half + (e - start);
+      off[u] = e + delta;
     }
     const uint64_t* rowseg =
         a.seg + (size_t)r * (ROWSEG ? (size_t)a.nchunks * a.segcap : (size_t)nseg * half);
