@@ -381,10 +381,10 @@ __global__ __launch_bounds__(kNT) void row_sample(BlockArgs a, uint16_t* samp) {
 // that keep every key (threshold -inf) and tiles crossing a row's
 // visibility limit take explicit compares instead.
 constexpr int kScrStride = 32;  // scratch words per lane: the step's 32 values
-// 16-byte piece q of a lane's scratch sits in slot q ^ ((lane / 2) % 8):
-// a lane's 128 bytes fill half of the 64 banks, so the 16 lanes a 128-bit
-// LDS access serves at once hit 16 distinct bank groups.
-CLSA_DEV int scr_slot(int q, int lane) { return q ^ ((lane >> 1) & 7); }
+// A wave's scratch is value-major: value i of lane l sits in word
+// i * 64 + l, so each lane stays in its own bank and the reads of hits at
+// different value indices never conflict.  (Lane-major 16-byte pieces made
+// those reads conflict and cost the filter 2 us.)
 
 // bf16 bits of -x, with x first rounded down to bf16 (toward -inf)
 CLSA_DEV uint16_t neg_bf16_floor(float x) {
@@ -429,8 +429,8 @@ CLSA_DEV uint32_t stage_hits(const f32x16_t& x0, const f32x16_t& x1, const SlabS
   return ~m;
 }
 
-// Spill the step's values of lanes with hits to scratch (each 32-key tile
-// only where it holds a hit), then append the hits (dd, position) to the
+// Spill the step's values of lanes with hits to the wave's scratch (each
+// 32-key tile only where it holds a hit), then append the hits (dd, position) to the
 // row's segment, up to four per lane per pass so that each pass waits on
 // LDS once.  Value i of a lane is key jl0 + i + (i & 28).
 CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, SlabState& st,
@@ -438,17 +438,12 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
   const int lane = lane_id();
   if ((hits & 0xffffu) != 0u) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      reinterpret_cast<float4*>(scr)[scr_slot(q, lane)] =
-          make_float4(x0[4 * q], x0[4 * q + 1], x0[4 * q + 2], x0[4 * q + 3]);
+    for (int i = 0; i < 16; ++i) scr[i * kWave + lane] = x0[i];
   }
   if ((hits >> 16) != 0u) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      reinterpret_cast<float4*>(scr)[scr_slot(4 + q, lane)] =
-          make_float4(x1[4 * q], x1[4 * q + 1], x1[4 * q + 2], x1[4 * q + 3]);
+    for (int i = 0; i < 16; ++i) scr[(16 + i) * kWave + lane] = x1[i];
   }
-  const int sw = ((lane >> 1) & 7) << 2;  // word i of the lane's values sits at i ^ sw
   while (__ballot(hits != 0u) != 0) {
     int idx[4];
     float dv[4];
@@ -459,7 +454,7 @@ CLSA_DEV void stage_emit(const f32x16_t& x0, const f32x16_t& x1, uint32_t hits, 
       h &= h - 1u;
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q] ^ sw];
+    for (int q = 0; q < 4; ++q) dv[q] = scr[idx[q] * kWave + lane];
     const uint32_t n = __popc(hits) - __popc(h);  // hits taken this pass (<= 4)
     // lanes l and l+32 hold the same row: one stream, the upper lane after
     // the lower one.  Swapping the wave's halves gives every lane the lower
@@ -517,7 +512,7 @@ void block_filter(BlockArgs a) {
   const int r_lo = g * a.rows_pg;
   const int r_hi = r_lo + a.rows_pg < a.M ? r_lo + a.rows_pg : a.M;
   const int64_t vis_hi = row_visible(a, b, r_hi - 1);  // visibility grows with m
-  float* scr = &scratch[w][lane * kScrStride];
+  float* scr = &scratch[w][0];  // the wave's scratch, value-major
   const bf16x8_t kone =  // constant operand of the threshold k-step: 1.0 in dim 0
       __builtin_bit_cast(bf16x8_t, u32x4_t{lane < 32 ? 0x3f80u : 0u, 0u, 0u, 0u});
   const int m0 = r_lo + 32 * w;
