@@ -293,6 +293,14 @@ def test_attn_bf16_generic_head_dim():
     _check_attn(*case)
 
 
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 2, 256), (16, 1, 256), (4, 4, 8), (2, 1, 16)])
+def test_attn_bf16_shapes_outside_the_fast_kernel(Hq, Hkv, D):
+    # group sizes the bf16 fast kernel does not take at D = 256 (16 query
+    # heads per KV head), and the smallest head dims, on the generic kernel
+    case = _attn_case(torch.bfloat16, 2, 2, 2, Hq, Hkv, D, 2500, 400, [400, 63, 1, 0], 27 + D)
+    _check_attn(*case)
+
+
 def test_attn_large_logits_stable():
     case = _attn_case(torch.bfloat16, 1, 2, 2, 32, 8, 128, 3000, 512, [512, 100], 24, qscale=40.0)
     _check_attn(*case)
