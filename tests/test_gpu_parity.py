@@ -205,6 +205,30 @@ def test_threshold_sets_and_overflow():
         assert np.array_equal(idx.cpu().numpy(), o_idx)
 
 
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 32), (torch.float32, 128),
+                                     (torch.bfloat16, 32)])
+def test_threshold_dtypes_and_index_widths(dtype, d):
+    # fp32 keys and the narrowest index head, with a context that ends
+    # inside a scan chunk
+    g = _cpu_gen(17 + d)
+    B, N = 3, 7001
+    K = torch.randn((B, N, d), generator=g).to(dtype)
+    q = (torch.randn((B, 1, d), generator=g) / math.sqrt(d)).to(dtype)
+    q_np, K_np = f64(q), f64(K)
+    n_ctx = [N, 5000, 1]
+    tau = np.zeros((B, 1), dtype=np.float32)
+    for b in range(B):
+        s = O.route_scores(q_np[b, 0], K_np[b], n_ctx[b])
+        tau[b, 0] = _tau_with_margin(s, min(200, n_ctx[b])) if n_ctx[b] > 1 else np.float32(s[0] - 1)
+    nc = torch.tensor(n_ctx, dtype=torch.int32, device=DEV)
+    for cap in (1024, 100):
+        idx, counts = clsa.route_threshold(q.to(DEV), K.to(DEV), torch.from_numpy(tau).to(DEV),
+                                           cap, n_ctx=nc)
+        o_idx, o_cnt = O.route_threshold(q_np, K_np, n_ctx, -1, tau, cap)
+        assert np.array_equal(counts.cpu().numpy(), o_cnt)
+        assert np.array_equal(idx.cpu().numpy(), o_idx)
+
+
 def test_threshold_ragged_context_and_prefill():
     g = _cpu_gen(16)
     B, M, N, d = 2, 9, 4100, 128
